@@ -1,6 +1,239 @@
 """BEAM masked-MoE layer forward on MI355X (gfx950): Python binding.
 
 The compute lives in the HIP library libbeam_moe.so (C-ABI declared in
-include/beam_moe.h).  This package only marshals torch tensors into that
-library's calls; it has no CPU fallback and raises if the library is missing.
+include/beam_moe.h).  This module only marshals torch tensors into that
+library's calls: it allocates outputs and workspace with torch, passes their
+device pointers and torch's current stream, and returns the tensors.  There is
+no CPU fallback: every call raises if the library is missing or the tensors
+are not on a GPU.
 """
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "BEAM_OK", "BEAM_EINVAL", "BEAM_EUNSUPPORTED", "BEAM_EWORKSPACE", "BEAM_EHIP",
+    "BEAM_F32", "BEAM_BF16", "BEAM_FORCE_DECODE", "BEAM_FORCE_PREFILL",
+    "STAGES", "BeamError", "lib", "library_path", "Desc", "Routing", "Sizes",
+    "make_desc", "query", "alloc_routing", "route", "forward", "MoELayer",
+]
+
+BEAM_OK, BEAM_EINVAL, BEAM_EUNSUPPORTED, BEAM_EWORKSPACE, BEAM_EHIP = 0, -1, -2, -3, -4
+BEAM_F32, BEAM_BF16 = 0, 1
+BEAM_FORCE_DECODE, BEAM_FORCE_PREFILL = 1, 2
+STAGES = ["router", "select", "scan", "scatter", "up", "down", "combine"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, "libbeam_moe.so")
+
+
+class BeamError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"beam_moe status {status}: {msg}")
+        self.status = status
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("I", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("block_m", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("tau", ctypes.c_float), ("reserved", ctypes.c_int32 * 3)]
+
+
+_ROUTING_FIELDS = ["gate_logits", "mask_logits", "topk_ids", "topk_weights", "mask", "g_hat",
+                   "masked_ids", "expert_counts", "expert_offsets", "sorted_pairs",
+                   "block_expert", "active_experts", "num_active"]
+
+
+class Routing(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in _ROUTING_FIELDS]
+
+
+class Sizes(ctypes.Structure):
+    _fields_ = [("workspace_bytes", ctypes.c_size_t), ("route_workspace_bytes", ctypes.c_size_t),
+                ("cap", ctypes.c_int64), ("n_blocks_cap", ctypes.c_int64),
+                ("block_m", ctypes.c_int32), ("path", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libbeam_moe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: build it with "
+                              "`python -m dynamic_expert_sparsity_amd.build`")
+        L = ctypes.CDLL(path)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        L.beam_moe_query.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Sizes)]
+        L.beam_moe_query.restype = ctypes.c_int
+        L.beam_moe_route.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, ctypes.POINTER(Routing),
+                                     vp, sz, vp]
+        L.beam_moe_route.restype = ctypes.c_int
+        L.beam_moe_forward.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, vp, vp, vp,
+                                       ctypes.POINTER(Routing), vp, sz, vp]
+        L.beam_moe_forward.restype = ctypes.c_int
+        L.beam_moe_forward_ex.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, vp, vp, vp,
+                                          ctypes.POINTER(Routing), vp, sz, vp, vp]
+        L.beam_moe_forward_ex.restype = ctypes.c_int
+        L.beam_moe_strerror.argtypes = [ctypes.c_int]
+        L.beam_moe_strerror.restype = ctypes.c_char_p
+        L.beam_moe_last_error.argtypes = []
+        L.beam_moe_last_error.restype = ctypes.c_char_p
+        L.beam_moe_version.argtypes = []
+        L.beam_moe_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != BEAM_OK:
+        L = lib()
+        raise BeamError(status, f"{L.beam_moe_strerror(status).decode()}: "
+                                f"{L.beam_moe_last_error().decode()}")
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return BEAM_F32
+    if dt == torch.bfloat16:
+        return BEAM_BF16
+    raise TypeError(f"unsupported dtype {dt}; use float32 or bfloat16")
+
+
+def make_desc(T, d, E, K, I, dtype, block_m=0, flags=0, tau=0.0) -> Desc:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return Desc(int(T), int(d), int(E), int(K), int(I), code, int(block_m), int(flags),
+                float(tau), (ctypes.c_int32 * 3)(0, 0, 0))
+
+
+def query(desc: Desc) -> dict:
+    s = Sizes()
+    _check(lib().beam_moe_query(ctypes.byref(desc), ctypes.byref(s)))
+    return {"workspace_bytes": s.workspace_bytes, "route_workspace_bytes": s.route_workspace_bytes,
+            "cap": s.cap, "n_blocks_cap": s.n_blocks_cap, "block_m": s.block_m, "path": s.path}
+
+
+def alloc_routing(desc: Desc, sizes: dict, device) -> dict:
+    T, E, K = desc.T, desc.E, desc.K
+    f32, i32 = torch.float32, torch.int32
+    mk = lambda shape, dt: torch.empty(shape, dtype=dt, device=device)  # noqa: E731
+    return {
+        "gate_logits": mk((T, E), f32), "mask_logits": mk((T, E), f32),
+        "topk_ids": mk((T, K), i32), "topk_weights": mk((T, K), f32),
+        "mask": mk((T, K), torch.uint8), "g_hat": mk((T, K), f32),
+        "masked_ids": mk((T, K), i32), "expert_counts": mk((E,), i32),
+        "expert_offsets": mk((E + 1,), i32), "sorted_pairs": mk((max(sizes["cap"], 1),), i32),
+        "block_expert": mk((max(sizes["n_blocks_cap"], 1),), i32),
+        "active_experts": mk((E,), i32), "num_active": mk((4,), i32),
+    }
+
+
+def _routing_struct(R: dict) -> Routing:
+    return Routing(*[R[n].data_ptr() for n in _ROUTING_FIELDS])
+
+
+def _gpu_tensor(name, t, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (the library has no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _stream_ptr(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+class MoELayer:
+    """A BEAM masked-MoE layer bound to fixed weights; reuses its output,
+    routing and workspace buffers across calls with the same T."""
+
+    def __init__(self, W_gate, W_mask, W_gu, W_dt, K, block_m=0, flags=0, tau=0.0):
+        E, d = W_gate.shape
+        self.dtype = W_gate.dtype
+        _gpu_tensor("W_gate", W_gate, self.dtype, (E, d))
+        _gpu_tensor("W_mask", W_mask, self.dtype, (E, d))
+        I = W_gu.shape[1] // 2
+        _gpu_tensor("W_gu", W_gu, self.dtype, (E, 2 * I, d))
+        _gpu_tensor("W_dt", W_dt, self.dtype, (E, d, I))
+        self.W_gate, self.W_mask, self.W_gu, self.W_dt = W_gate, W_mask, W_gu, W_dt
+        self.d, self.E, self.K, self.I = d, E, int(K), I
+        self.block_m, self.flags, self.tau = block_m, flags, tau
+        self._T = None
+
+    def _prepare(self, T):
+        if self._T == T:
+            return
+        dev = self.W_gate.device
+        self.desc = make_desc(T, self.d, self.E, self.K, self.I, self.dtype, self.block_m,
+                              self.flags, self.tau)
+        self.sizes = query(self.desc)
+        self.routing = alloc_routing(self.desc, self.sizes, dev)
+        self._rs = _routing_struct(self.routing)
+        self.ws = torch.empty(max(self.sizes["workspace_bytes"], 256), dtype=torch.uint8, device=dev)
+        self.y = torch.empty((T, self.d), dtype=self.dtype, device=dev)
+        self._T = T
+
+    def forward(self, x, stream=None, events=None):
+        """Run the layer on x [T, d]; returns (y, routing dict).  The returned
+        tensors are this layer's buffers and are overwritten by the next call.
+        events: optional list of len(STAGES)+1 raw hipEvent_t handles."""
+        _gpu_tensor("x", x, self.dtype)
+        T = x.shape[0]
+        self._prepare(T)
+        ev = None
+        if events is not None:
+            if len(events) != len(STAGES) + 1:
+                raise ValueError("need len(STAGES) + 1 events")
+            ev = (ctypes.c_void_p * len(events))(*events)
+        _check(lib().beam_moe_forward_ex(
+            ctypes.byref(self.desc), x.data_ptr(), self.W_gate.data_ptr(), self.W_mask.data_ptr(),
+            self.W_gu.data_ptr(), self.W_dt.data_ptr(), self.y.data_ptr(), ctypes.byref(self._rs),
+            self.ws.data_ptr(), self.ws.numel(), _stream_ptr(stream), ev))
+        return self.y, self.routing
+
+    __call__ = forward
+
+
+def route(x, W_gate, W_mask, K, block_m=0, flags=0, tau=0.0, stream=None) -> dict:
+    """beam_moe_route: routing tensors for x (new buffers)."""
+    E, d = W_gate.shape
+    _gpu_tensor("x", x, W_gate.dtype)
+    _gpu_tensor("W_gate", W_gate, x.dtype, (E, d))
+    _gpu_tensor("W_mask", W_mask, x.dtype, (E, d))
+    T = x.shape[0]
+    desc = make_desc(T, d, E, K, 32, x.dtype, block_m, flags, tau)
+    sizes = query(desc)
+    R = alloc_routing(desc, sizes, x.device)
+    ws = torch.empty(max(sizes["route_workspace_bytes"], 256), dtype=torch.uint8, device=x.device)
+    _check(lib().beam_moe_route(ctypes.byref(desc), x.data_ptr(), W_gate.data_ptr(),
+                                W_mask.data_ptr(), ctypes.byref(_routing_struct(R)),
+                                ws.data_ptr(), ws.numel(), _stream_ptr(stream)))
+    R["_ws"] = ws  # keep alive until the stream has used it
+    return R
+
+
+def forward(x, W_gate, W_mask, W_gu, W_dt, K, block_m=0, flags=0, tau=0.0, stream=None):
+    """beam_moe_forward: (y, routing) for x (new buffers)."""
+    layer = MoELayer(W_gate, W_mask, W_gu, W_dt, K, block_m, flags, tau)
+    y, R = layer.forward(x, stream)
+    R = dict(R)
+    R["_ws"] = layer.ws
+    return y, R

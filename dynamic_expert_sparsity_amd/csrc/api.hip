@@ -1,0 +1,265 @@
+// C-ABI of libbeam_moe: argument validation, the launch plan, workspace
+// carve-up and the stage sequence (declared in include/beam_moe.h).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "beam_moe.h"
+#include "kernels.h"
+
+using namespace beam;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool aligned(const void *p, size_t a) { return p && (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Validate a descriptor and build the plan (host only).
+int make_plan(const beam_moe_desc *desc, Plan &p) {
+    if (!desc) return fail(BEAM_EINVAL, "desc is NULL");
+    const beam_moe_desc &D = *desc;
+    if (D.T < 0 || D.d <= 0 || D.E <= 0 || D.K <= 0 || D.I <= 0)
+        return fail(BEAM_EINVAL, "sizes must satisfy T >= 0 and d, E, K, I > 0 (T=%d d=%d E=%d K=%d I=%d)",
+                    D.T, D.d, D.E, D.K, D.I);
+    if (D.K > D.E) return fail(BEAM_EINVAL, "K=%d exceeds E=%d", D.K, D.E);
+    if (D.dtype != BEAM_F32 && D.dtype != BEAM_BF16)
+        return fail(BEAM_EINVAL, "dtype %d is neither BEAM_F32 nor BEAM_BF16", D.dtype);
+    if (D.block_m != 0 && D.block_m != 16 && D.block_m != 32 && D.block_m != 64 && D.block_m != 128)
+        return fail(BEAM_EINVAL, "block_m %d is not 0, 16, 32, 64 or 128", D.block_m);
+    if (D.flags & ~(BEAM_FORCE_DECODE | BEAM_FORCE_PREFILL))
+        return fail(BEAM_EINVAL, "unknown flag bits 0x%x", D.flags);
+    if ((D.flags & BEAM_FORCE_DECODE) && (D.flags & BEAM_FORCE_PREFILL))
+        return fail(BEAM_EINVAL, "BEAM_FORCE_DECODE and BEAM_FORCE_PREFILL are exclusive");
+    if (!(D.tau == 0.f || (D.tau > 0.f && D.tau < 1.f)))
+        return fail(BEAM_EINVAL, "tau must be 0 (meaning 0.5) or lie in (0, 1)");
+    if (D.reserved[0] || D.reserved[1] || D.reserved[2])
+        return fail(BEAM_EINVAL, "reserved fields must be 0");
+
+    if (D.E > 256) return fail(BEAM_EUNSUPPORTED, "E=%d > 256", D.E);
+    if (D.K > 64) return fail(BEAM_EUNSUPPORTED, "K=%d > 64", D.K);
+    if (D.dtype == BEAM_BF16 && (D.d % 128 != 0 || D.I % 32 != 0))
+        return fail(BEAM_EUNSUPPORTED, "bf16 layer needs d %% 128 == 0 and I %% 32 == 0 (d=%d I=%d)",
+                    D.d, D.I);
+    if (D.flags & BEAM_FORCE_PREFILL)
+        return fail(BEAM_EUNSUPPORTED, "the tiled prefill path is not available in this build");
+    const long long TK = (long long)D.T * D.K;
+    if (TK > (1ll << 30)) return fail(BEAM_EUNSUPPORTED, "T*K=%lld too large", TK);
+
+    p.T = D.T; p.d = D.d; p.E = D.E; p.K = D.K; p.I = D.I;
+    p.dtype = D.dtype;
+    p.path = 0;
+    p.bm = D.block_m ? D.block_m : 16;
+    const float tau = D.tau == 0.f ? 0.5f : D.tau;
+    // m = [sigmoid(z) >= tau]  <=>  z >= ln(tau / (1 - tau)); exactly 0 at tau = 0.5
+    p.thr = tau == 0.5f ? 0.f : (float)std::log((double)tau / (1.0 - (double)tau));
+
+    // router logits: token tile, and splits of d so that small T still
+    // spreads the 2*E*d weight read over many workgroups
+    p.r_tt = D.T <= 64 ? 16 : 64;
+    if (p.dtype == BEAM_BF16) {
+        const long long tiles = (long long)((D.T + p.r_tt - 1) / p.r_tt) * ((2 * D.E + 63) / 64);
+        long long splits = 1024 / (tiles > 0 ? tiles : 1);
+        const long long max_splits = D.d / 128;
+        if (splits > max_splits) splits = max_splits;
+        if (splits < 1) splits = 1;
+        int dchunk = (int)((D.d + splits - 1) / splits);
+        dchunk = (dchunk + 31) / 32 * 32;
+        p.r_dchunk = dchunk;
+        p.r_splits = (D.d + dchunk - 1) / dchunk;
+    } else {
+        p.r_splits = 1;
+        p.r_dchunk = D.d;
+    }
+    p.s_ts = 64;
+    p.n_tiles = (D.T + 63) / 64;
+    p.max_active = (int)(TK < D.E ? TK : D.E);
+    const long long cap_raw = TK + (long long)p.max_active * (p.bm - 1);
+    p.cap = (cap_raw + p.bm - 1) / p.bm * p.bm;
+    p.n_blocks_cap = p.cap / p.bm;
+
+    const size_t elt = p.dtype == BEAM_BF16 ? 2 : 4;
+    size_t off = 0;
+    p.off_partial = off;   off = align_up(off + (size_t)p.r_splits * D.T * 2 * D.E * 4, 256);
+    p.off_tile_mask = off; off = align_up(off + (size_t)p.n_tiles * D.E * 8, 256);
+    p.off_tile_base = off; off = align_up(off + (size_t)p.n_tiles * D.E * 4, 256);
+    p.off_pair_pos = off;  off = align_up(off + (size_t)TK * 4, 256);
+    p.route_bytes = off;
+    p.off_h = off;         off = align_up(off + (size_t)p.cap * D.I * elt, 256);
+    p.off_o = off;         off = align_up(off + (size_t)p.cap * D.d * elt, 256);
+    p.total_bytes = off;
+    return BEAM_OK;
+}
+
+int check_routing(const beam_moe_routing *o, Routing &r) {
+    if (!o) return fail(BEAM_EINVAL, "routing struct is NULL");
+    const void *ptrs[] = {o->gate_logits,  o->mask_logits,    o->topk_ids,     o->topk_weights,
+                          o->g_hat,        o->masked_ids,     o->expert_counts, o->expert_offsets,
+                          o->sorted_pairs, o->block_expert,   o->active_experts, o->num_active};
+    const char *names[] = {"gate_logits",  "mask_logits",  "topk_ids",      "topk_weights",
+                           "g_hat",        "masked_ids",   "expert_counts", "expert_offsets",
+                           "sorted_pairs", "block_expert", "active_experts", "num_active"};
+    for (size_t i = 0; i < sizeof ptrs / sizeof ptrs[0]; ++i)
+        if (!aligned(ptrs[i], 4)) return fail(BEAM_EINVAL, "routing.%s is NULL or not 4-byte aligned", names[i]);
+    if (!o->mask) return fail(BEAM_EINVAL, "routing.mask is NULL");
+    r.gate_logits = o->gate_logits; r.mask_logits = o->mask_logits;
+    r.topk_ids = o->topk_ids; r.topk_weights = o->topk_weights; r.mask = o->mask;
+    r.g_hat = o->g_hat; r.masked_ids = o->masked_ids;
+    r.expert_counts = o->expert_counts; r.expert_offsets = o->expert_offsets;
+    r.sorted_pairs = o->sorted_pairs; r.block_expert = o->block_expert;
+    r.active_experts = o->active_experts; r.num_active = o->num_active;
+    return BEAM_OK;
+}
+
+Work carve(const Plan &p, void *ws) {
+    char *b = static_cast<char *>(ws);
+    Work w;
+    w.partial = reinterpret_cast<float *>(b + p.off_partial);
+    w.tile_mask = reinterpret_cast<uint64_t *>(b + p.off_tile_mask);
+    w.tile_base = reinterpret_cast<int32_t *>(b + p.off_tile_base);
+    w.pair_pos = reinterpret_cast<int32_t *>(b + p.off_pair_pos);
+    w.h = b + p.off_h;
+    w.o = b + p.off_o;
+    return w;
+}
+
+struct Events {
+    hipEvent_t *ev;
+    hipStream_t s;
+    hipError_t mark(int i) const { return ev ? hipEventRecord(ev[i], s) : hipSuccess; }
+};
+
+#define BEAM_TRY(expr, stage)                                                             \
+    do {                                                                                  \
+        hipError_t e_ = (expr);                                                           \
+        if (e_ != hipSuccess)                                                             \
+            return fail(BEAM_EHIP, "%s: %s", stage, hipGetErrorString(e_));               \
+    } while (0)
+
+int enqueue_route(const Plan &p, const void *x, const void *Wg, const void *Wm, const Routing &r,
+                  const Work &w, hipStream_t s, const Events &ev) {
+    BEAM_TRY(ev.mark(BEAM_STAGE_ROUTER), "event");
+    BEAM_TRY(launch_router_logits(p, x, Wg, Wm, w, s), "router logits");
+    BEAM_TRY(ev.mark(BEAM_STAGE_SELECT), "event");
+    BEAM_TRY(launch_select(p, r, w, s), "select");
+    BEAM_TRY(ev.mark(BEAM_STAGE_SCAN), "event");
+    BEAM_TRY(launch_scan(p, r, w, s), "compaction scan");
+    BEAM_TRY(ev.mark(BEAM_STAGE_SCATTER), "event");
+    BEAM_TRY(launch_scatter(p, r, w, s), "compaction scatter");
+    return BEAM_OK;
+}
+
+int check_inputs(const void *x, const void *Wg, const void *Wm) {
+    if (!aligned(x, 16)) return fail(BEAM_EINVAL, "x is NULL or not 16-byte aligned");
+    if (!aligned(Wg, 16)) return fail(BEAM_EINVAL, "W_gate is NULL or not 16-byte aligned");
+    if (!aligned(Wm, 16)) return fail(BEAM_EINVAL, "W_mask is NULL or not 16-byte aligned");
+    return BEAM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int beam_moe_query(const beam_moe_desc *desc, beam_moe_sizes *out) {
+    Plan p;
+    int rc = make_plan(desc, p);
+    if (rc) return rc;
+    if (!out) return fail(BEAM_EINVAL, "sizes output is NULL");
+    out->workspace_bytes = p.total_bytes;
+    out->route_workspace_bytes = p.route_bytes;
+    out->cap = p.cap;
+    out->n_blocks_cap = p.n_blocks_cap;
+    out->block_m = p.bm;
+    out->path = p.path;
+    return BEAM_OK;
+}
+
+int beam_moe_route(const beam_moe_desc *desc, const void *x, const void *W_gate,
+                   const void *W_mask, const beam_moe_routing *out, void *ws, size_t ws_bytes,
+                   hipStream_t stream) {
+    Plan p;
+    int rc = make_plan(desc, p);
+    if (rc) return rc;
+    if (p.T == 0) return BEAM_OK;
+    if ((rc = check_inputs(x, W_gate, W_mask))) return rc;
+    Routing r;
+    if ((rc = check_routing(out, r))) return rc;
+    if (!aligned(ws, 16)) return fail(BEAM_EINVAL, "workspace is NULL or not 16-byte aligned");
+    if (ws_bytes < p.route_bytes)
+        return fail(BEAM_EWORKSPACE, "workspace has %zu bytes, route needs %zu", ws_bytes, p.route_bytes);
+    return enqueue_route(p, x, W_gate, W_mask, r, carve(p, ws), stream, Events{nullptr, stream});
+}
+
+int beam_moe_forward_ex(const beam_moe_desc *desc, const void *x, const void *W_gate,
+                        const void *W_mask, const void *W_gu, const void *W_dt, void *y,
+                        const beam_moe_routing *out, void *ws, size_t ws_bytes,
+                        hipStream_t stream, hipEvent_t *stage_events) {
+    Plan p;
+    int rc = make_plan(desc, p);
+    if (rc) return rc;
+    if (p.T == 0) return BEAM_OK;
+    if ((rc = check_inputs(x, W_gate, W_mask))) return rc;
+    if (!aligned(W_gu, 16)) return fail(BEAM_EINVAL, "W_gu is NULL or not 16-byte aligned");
+    if (!aligned(W_dt, 16)) return fail(BEAM_EINVAL, "W_dt is NULL or not 16-byte aligned");
+    if (!aligned(y, 16)) return fail(BEAM_EINVAL, "y is NULL or not 16-byte aligned");
+    Routing r;
+    if ((rc = check_routing(out, r))) return rc;
+    if (!aligned(ws, 16)) return fail(BEAM_EINVAL, "workspace is NULL or not 16-byte aligned");
+    if (ws_bytes < p.total_bytes)
+        return fail(BEAM_EWORKSPACE, "workspace has %zu bytes, forward needs %zu", ws_bytes, p.total_bytes);
+    if (stage_events)
+        for (int i = 0; i <= BEAM_NUM_STAGES; ++i)
+            if (!stage_events[i]) return fail(BEAM_EINVAL, "stage_events[%d] is NULL", i);
+
+    const Work w = carve(p, ws);
+    const Events ev{stage_events, stream};
+    if ((rc = enqueue_route(p, x, W_gate, W_mask, r, w, stream, ev))) return rc;
+    BEAM_TRY(ev.mark(BEAM_STAGE_UP), "event");
+    BEAM_TRY(launch_expert_up(p, x, W_gu, r, w, stream), "expert up");
+    BEAM_TRY(ev.mark(BEAM_STAGE_DOWN), "event");
+    BEAM_TRY(launch_expert_down(p, W_dt, r, w, stream), "expert down");
+    BEAM_TRY(ev.mark(BEAM_STAGE_COMBINE), "event");
+    BEAM_TRY(launch_combine(p, r, w, y, stream), "combine");
+    BEAM_TRY(ev.mark(BEAM_NUM_STAGES), "event");
+    return BEAM_OK;
+}
+
+int beam_moe_forward(const beam_moe_desc *desc, const void *x, const void *W_gate,
+                     const void *W_mask, const void *W_gu, const void *W_dt, void *y,
+                     const beam_moe_routing *out, void *ws, size_t ws_bytes, hipStream_t stream) {
+    return beam_moe_forward_ex(desc, x, W_gate, W_mask, W_gu, W_dt, y, out, ws, ws_bytes, stream,
+                               nullptr);
+}
+
+const char *beam_moe_strerror(int status) {
+    switch (status) {
+        case BEAM_OK: return "ok";
+        case BEAM_EINVAL: return "invalid argument";
+        case BEAM_EUNSUPPORTED: return "unsupported configuration";
+        case BEAM_EWORKSPACE: return "workspace too small";
+        case BEAM_EHIP: return "HIP launch error";
+        default: return "unknown status";
+    }
+}
+
+const char *beam_moe_last_error(void) { return g_last_error.c_str(); }
+
+const char *beam_moe_version(void) { return "0.1.0"; }
+
+}  // extern "C"

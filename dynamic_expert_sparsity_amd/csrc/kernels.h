@@ -1,0 +1,63 @@
+// Internal launch interface between the C-ABI layer (api.hip) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace beam {
+
+// Everything the launchers need, fixed on the host from the descriptor.
+struct Plan {
+    int T, d, E, K, I;
+    int dtype;          // 0 f32, 1 bf16
+    int bm;             // block_m
+    int path;           // 0 streaming (decode), 1 tiled (prefill)
+    float thr;          // mask logit threshold: m = [z >= thr]
+    // router logits
+    int r_tt;           // tokens per router tile (multiple of 16)
+    int r_splits;       // splits of d (partial sums reduced in fixed order)
+    int r_dchunk;       // d per split (multiple of 32)
+    // select / compaction
+    int s_ts;           // tokens per select tile (64)
+    int n_tiles;        // ceil(T / s_ts)
+    long long cap;          // sorted_pairs capacity
+    long long n_blocks_cap; // block_expert capacity
+    int max_active;     // host upper bound on experts with >= 1 active pair
+    // workspace carve-up (byte offsets) and totals
+    size_t off_partial, off_tile_mask, off_tile_base, off_pair_pos, off_h, off_o;
+    size_t route_bytes, total_bytes;
+};
+
+struct Routing {
+    float *gate_logits, *mask_logits;
+    int32_t *topk_ids;
+    float *topk_weights;
+    uint8_t *mask;
+    float *g_hat;
+    int32_t *masked_ids;
+    int32_t *expert_counts, *expert_offsets, *sorted_pairs, *block_expert;
+    int32_t *active_experts, *num_active;
+};
+
+struct Work {  // workspace views
+    float *partial;
+    uint64_t *tile_mask;
+    int32_t *tile_base;
+    int32_t *pair_pos;
+    void *h;
+    void *o;
+};
+
+hipError_t launch_router_logits(const Plan &p, const void *x, const void *Wg, const void *Wm,
+                                const Work &w, hipStream_t s);
+hipError_t launch_select(const Plan &p, const Routing &r, const Work &w, hipStream_t s);
+hipError_t launch_scan(const Plan &p, const Routing &r, const Work &w, hipStream_t s);
+hipError_t launch_scatter(const Plan &p, const Routing &r, const Work &w, hipStream_t s);
+hipError_t launch_expert_up(const Plan &p, const void *x, const void *W_gu, const Routing &r,
+                            const Work &w, hipStream_t s);
+hipError_t launch_expert_down(const Plan &p, const void *W_dt, const Routing &r,
+                              const Work &w, hipStream_t s);
+hipError_t launch_combine(const Plan &p, const Routing &r, const Work &w, void *y,
+                          hipStream_t s);
+
+}  // namespace beam

@@ -1,0 +1,164 @@
+/*
+ * beam_moe.h -- C-ABI of the BEAM masked-MoE layer forward on MI355X (gfx950).
+ *
+ * The layer (BEAM paper, "Binary Expert Activation Masking for Dynamic Routing
+ * in MoE", section 3.2, Eq. 4-8):
+ *   r = x W_gate^T, Top-K of r, g = Softmax over the K kept logits   (Eq. 4)
+ *   z = x W_mask^T, m = [sigmoid(z) >= 0.5] = [z >= 0]                (Eq. 5-6)
+ *   g_hat = g * m, no renormalisation, no minimum active count        (Eq. 7)
+ *   y = sum_k g_hat_k * E_{id_k}(x), E(x) = (SiLU(x Wg) * (x Wu)) Wd  (Eq. 8, Eq. 3)
+ * Masked slots carry the expert id -1 and are left out of the per-expert
+ * counts, so masked (token, expert) pairs are never scheduled (the vLLM
+ * integration described in section 5 of the news article on the paper).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller, row-major,
+ *     16-byte aligned (tensor inputs/outputs) or 4-byte aligned (routing
+ *     buffers).  The library never allocates, frees or retains memory, never
+ *     synchronises the stream and never reads device memory on the host.
+ *   - Work is enqueued on `stream` (0 = the null stream) and runs
+ *     asynchronously; a return value of 0 means "enqueued".
+ *   - Errors are negative and are detected on the host BEFORE anything is
+ *     enqueued, except BEAM_EHIP (a launch failed; earlier stages of the same
+ *     call may have been enqueued).  beam_moe_last_error() gives the message
+ *     for the calling thread.
+ *   - T = 0 is a valid call that enqueues nothing.
+ *   - The library holds no mutable global state; calls from several threads
+ *     are safe as long as they use distinct output and workspace buffers.
+ *
+ * Storage layouts (dtype = BEAM_F32: float everywhere; BEAM_BF16: bfloat16):
+ *   x       [T, d]
+ *   W_gate  [E, d]      one row per expert (the transpose of the paper's
+ *   W_mask  [E, d]      R in R^{d x N} and W_m in R^{d_h x N}; nn.Linear layout)
+ *   W_gu    [E, 2I, d]  rows 0..I-1: gate projection (Eq. 3 "W_gate^(i)"),
+ *                       rows I..2I-1: up projection; each row is one
+ *                       intermediate unit
+ *   W_dt    [E, d, I]   down projection, one row per output channel
+ *   y       [T, d]
+ */
+#ifndef BEAM_MOE_H
+#define BEAM_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define BEAM_OK            0
+#define BEAM_EINVAL       (-1) /* null/misaligned pointer, bad sizes, K > E ...   */
+#define BEAM_EUNSUPPORTED (-2) /* valid but outside kernel coverage (see query)   */
+#define BEAM_EWORKSPACE   (-3) /* workspace too small                              */
+#define BEAM_EHIP         (-4) /* a HIP launch failed                              */
+
+/* dtypes */
+#define BEAM_F32  0
+#define BEAM_BF16 1
+
+/* desc.flags */
+#define BEAM_FORCE_DECODE   (1u << 0) /* weight-streaming expert kernels          */
+#define BEAM_FORCE_PREFILL  (1u << 1) /* LDS-tiled grouped-GEMM expert kernels     */
+
+/* stage ids for the optional per-stage events of beam_moe_forward_ex */
+#define BEAM_STAGE_ROUTER   0 /* a1: router logits (both routers)                 */
+#define BEAM_STAGE_SELECT   1 /* a2-a3: top-K, softmax, mask, g_hat, -1 ids       */
+#define BEAM_STAGE_SCAN     2 /* a4: per-expert counts, offsets, lists metadata   */
+#define BEAM_STAGE_SCATTER  3 /* a4: pairs into per-expert sorted lists           */
+#define BEAM_STAGE_UP       4 /* a5: expert gate/up projections + SiLU * up       */
+#define BEAM_STAGE_DOWN     5 /* a6: expert down projection                       */
+#define BEAM_STAGE_COMBINE  6 /* a7: masked weighted sum                          */
+#define BEAM_NUM_STAGES     7
+
+typedef struct beam_moe_desc {
+    int32_t  T;        /* tokens                                   (>= 0)      */
+    int32_t  d;        /* hidden size                              (> 0)       */
+    int32_t  E;        /* routed experts, the paper's N            (> 0)       */
+    int32_t  K;        /* top-K                                    (1..E)      */
+    int32_t  I;        /* expert intermediate size                 (> 0)       */
+    int32_t  dtype;    /* BEAM_F32 or BEAM_BF16                                */
+    int32_t  block_m;  /* 0 = library picks; else 16, 32, 64 or 128            */
+    uint32_t flags;    /* BEAM_FORCE_*                                         */
+    float    tau;      /* mask threshold on sigmoid(z); 0 means 0.5 (Eq. 6).
+                          Evaluated exactly as z >= ln(tau / (1 - tau)).       */
+    int32_t  reserved[3]; /* must be 0                                         */
+} beam_moe_desc;
+
+/* Routing outputs (all device pointers, caller-owned; sizes from
+ * beam_moe_query).  A "pair" is p = t*K + k. */
+typedef struct beam_moe_routing {
+    float   *gate_logits;    /* [T, E]  r (fp32 accumulate)                      */
+    float   *mask_logits;    /* [T, E]  z                                        */
+    int32_t *topk_ids;       /* [T, K]  descending r, equal r -> lower id first  */
+    float   *topk_weights;   /* [T, K]  g (Eq. 4), before the mask               */
+    uint8_t *mask;           /* [T, K]  m in {0, 1} (Eq. 6)                      */
+    float   *g_hat;          /* [T, K]  g * m (Eq. 7)                            */
+    int32_t *masked_ids;     /* [T, K]  topk_ids, or -1 where m = 0              */
+    int32_t *expert_counts;  /* [E]     active pairs per expert                  */
+    int32_t *expert_offsets; /* [E+1]   exclusive scan of counts rounded up to
+                                        block_m                                  */
+    int32_t *sorted_pairs;   /* [cap]   per expert: its pair ids ascending, then
+                                        the pad value T*K up to a multiple of
+                                        block_m; entries >= num_padded unused    */
+    int32_t *block_expert;   /* [cap/block_m] expert of each block_m block       */
+    int32_t *active_experts; /* [E]     experts with count >= 1, ascending;
+                                        entries >= n_active_experts unused       */
+    int32_t *num_active;     /* [4]     {P = active pairs, num_padded,
+                                         n_active_experts, n_blocks}             */
+} beam_moe_routing;
+
+/* Sizes for a descriptor (host only, enqueues nothing). */
+typedef struct beam_moe_sizes {
+    size_t  workspace_bytes;   /* bytes needed by beam_moe_forward              */
+    size_t  route_workspace_bytes; /* bytes needed by beam_moe_route            */
+    int64_t cap;               /* length of sorted_pairs                        */
+    int64_t n_blocks_cap;      /* length of block_expert                        */
+    int32_t block_m;           /* block size in effect                          */
+    int32_t path;              /* 0 = decode (streaming), 1 = prefill (tiled)   */
+} beam_moe_sizes;
+
+/* beam_moe_query: validate `desc` and fill `out`.
+ * Returns BEAM_OK, BEAM_EINVAL or BEAM_EUNSUPPORTED. */
+int beam_moe_query(const beam_moe_desc *desc, beam_moe_sizes *out);
+
+/* beam_moe_route: Eq. 4-7 and the grouping of active pairs (news article,
+ * section 5: masked ids -> -1, excluded from the counts).
+ * x, W_gate, W_mask: see the layouts above.  Writes every field of `out`.
+ * ws: device workspace of at least sizes.route_workspace_bytes bytes. */
+int beam_moe_route(const beam_moe_desc *desc, const void *x, const void *W_gate,
+                   const void *W_mask, const beam_moe_routing *out, void *ws,
+                   size_t ws_bytes, hipStream_t stream);
+
+/* beam_moe_forward: the whole layer, Eq. 3-8.  Writes y [T, d] and every
+ * routing field.  ws: at least sizes.workspace_bytes bytes. */
+int beam_moe_forward(const beam_moe_desc *desc, const void *x, const void *W_gate,
+                     const void *W_mask, const void *W_gu, const void *W_dt, void *y,
+                     const beam_moe_routing *out, void *ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/* beam_moe_forward_ex: beam_moe_forward plus optional per-stage events.
+ * stage_events: NULL, or BEAM_NUM_STAGES + 1 events created by the caller;
+ * event i is recorded on `stream` just before stage i is enqueued and event
+ * BEAM_NUM_STAGES after the last stage (a stage that the chosen path fuses
+ * into another one, or skips, has equal start and end events). */
+int beam_moe_forward_ex(const beam_moe_desc *desc, const void *x, const void *W_gate,
+                        const void *W_mask, const void *W_gu, const void *W_dt,
+                        void *y, const beam_moe_routing *out, void *ws,
+                        size_t ws_bytes, hipStream_t stream,
+                        hipEvent_t *stage_events);
+
+/* Text for a status code (static storage). */
+const char *beam_moe_strerror(int status);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char *beam_moe_last_error(void);
+
+/* Library version, e.g. "0.1.0". */
+const char *beam_moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BEAM_MOE_H */

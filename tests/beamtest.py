@@ -1,0 +1,113 @@
+"""Shared helpers for the GPU parity tests: run the HIP layer through the
+C-ABI binding, and compare with the fp64 oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import dynamic_expert_sparsity_amd as B
+from dynamic_expert_sparsity_amd import synth
+
+ROUTE_KEYS_EXACT = ["topk_ids", "mask", "masked_ids", "counts", "offsets", "active_experts",
+                    "num_active"]
+
+
+def need_gpu():
+    import pytest
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test run without a GPU")
+
+
+class ExpertView:
+    """Lazy per-expert float32 host copies of a device weight tensor."""
+
+    def __init__(self, W):
+        self.W = W
+
+    def __getitem__(self, e):
+        return self.W[e].float().cpu().numpy()
+
+
+def host(t):
+    return t.float().cpu().numpy() if t.dtype in (torch.bfloat16, torch.float16) else t.cpu().numpy()
+
+
+def run(L, K, block_m=0, flags=0, tau=0.0, x=None):
+    layer = B.MoELayer(L["W_gate"], L["W_mask"], L["W_gu"], L["W_dt"], K, block_m=block_m,
+                       flags=flags, tau=tau)
+    y, R = layer(L["x"] if x is None else x)
+    torch.cuda.synchronize()
+    out = {k: v.cpu() for k, v in R.items()}
+    return y.float().cpu().numpy(), out, layer
+
+
+def gpu_routing_host(R):
+    n = R["num_active"].numpy()
+    return {
+        "gate_logits": R["gate_logits"].numpy(), "mask_logits": R["mask_logits"].numpy(),
+        "topk_ids": R["topk_ids"].numpy(), "topk_weights": R["topk_weights"].numpy(),
+        "mask": R["mask"].numpy(), "g_hat": R["g_hat"].numpy(),
+        "masked_ids": R["masked_ids"].numpy(), "counts": R["expert_counts"].numpy(),
+        "offsets": R["expert_offsets"].numpy(),
+        "sorted_pairs": R["sorted_pairs"].numpy()[:n[1]],
+        "block_expert": R["block_expert"].numpy()[:n[3]],
+        "active_experts": R["active_experts"].numpy()[:n[2]], "num_active": n,
+    }
+
+
+def check_routing_exact(G, K, block_m, tau=0.5):
+    """Every discrete routing output must equal the oracle's decisions on the
+    GPU's own float32 logits, bit for bit; g and g_hat to float32 rounding."""
+    O = oracle.route_from_logits(G["gate_logits"], G["mask_logits"], K, block_m, tau)
+    for k in ROUTE_KEYS_EXACT:
+        if k == "num_active":
+            want = np.array([O["num_active"][0], O["num_active"][1], len(O["active_experts"]),
+                             len(O["block_expert"])])
+        else:
+            want = O[k]
+        np.testing.assert_array_equal(G[k], want, err_msg=k)
+    np.testing.assert_array_equal(G["sorted_pairs"], O["sorted_pairs"], err_msg="sorted_pairs")
+    np.testing.assert_array_equal(G["block_expert"], O["block_expert"], err_msg="block_expert")
+    np.testing.assert_allclose(G["topk_weights"], O["topk_weights"], rtol=2e-6, atol=1e-7)
+    np.testing.assert_allclose(G["g_hat"], O["g_hat"], rtol=2e-6, atol=1e-7)
+    return O
+
+
+def check_logits(G, L, rel=1e-3):
+    r, z = oracle.router_logits(host(L["x"]), host(L["W_gate"]), host(L["W_mask"]))
+    for name, got, ref in (("gate", G["gate_logits"], r), ("mask", G["mask_logits"], z)):
+        scale = max(np.abs(ref).max(), 1e-30)
+        assert np.abs(got - ref).max() <= rel * scale, f"{name} logits max abs err"
+        assert np.linalg.norm(got - ref) <= rel * max(np.linalg.norm(ref), 1e-30), f"{name} rel-L2"
+    return r, z
+
+
+def rel_l2(a, b):
+    nb = np.linalg.norm(b)
+    if nb == 0:
+        return float(np.linalg.norm(a))
+    return float(np.linalg.norm(a - b) / nb)
+
+
+def check_y(y, L, K, O, tol, tokens=None):
+    """y against the oracle's Eq. 8 on the same routing decisions."""
+    rows = np.arange(y.shape[0]) if tokens is None else np.asarray(tokens)
+    ref = oracle.forward(host(L["x"]), None, None, ExpertView(L["W_gu"]), ExpertView(L["W_dt"]),
+                         K, routing=O, tokens=rows)
+    err = rel_l2(y[rows], ref)
+    assert err <= tol, f"y rel-L2 {err:.3e} > {tol}"
+    # tokens with no active slot are exactly zero
+    dead = rows[np.asarray(O["mask"])[rows].sum(axis=1) == 0]
+    assert np.all(y[dead] == 0.0)
+    return err
+
+
+def sample_tokens(T, n, seed=0):
+    if T <= n:
+        return np.arange(T)
+    return np.sort(np.random.default_rng(seed).choice(T, n, replace=False))
+
+
+def layer(shape, T, **kw):
+    return synth.make_layer(shape, T, device="cuda", **kw)
