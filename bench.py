@@ -1,0 +1,326 @@
+#!/usr/bin/env python3
+"""Benchmark of the BEAM masked-MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one call of the whole layer (router logits, Top-K/softmax/mask,
+compaction, expert up and down projections on the active pairs, combine) on
+one batch of T tokens, with the inputs already resident in HBM.  The headline
+workload is the Qwen3-30B-A3B-shaped layer (d=2048, E=128 experts, top-8,
+I=768, bf16) at decode, T=256 tokens, mask bias b=-1.04 (expected keep rate
+Phi(-1.04) = 0.149, the paper's ~85% FLOP cut).  Steps rotate over several
+independently drawn weight sets (as the layers of a model would) so that the
+256 MB infinity cache cannot serve repeated weights.
+
+Printed on one JSON line: tokens/s (value), ms per step, the HBM roofline of
+the dominant kernel (per-stage HIP events recorded on the launch stream
+inside the timed steps), the whole-layer HBM fraction, the same kernels with
+the mask forced all-ones (W_mask = 0, plain Top-K), a sweep over the decode
+batch sizes, and the fp64 oracle timed on this host's cores on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, vendor figure
+METRIC = "masked-MoE layer tok/s + HBM GB/s (decode) / MFMA % (prefill), E128 K8"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--T", type=int, default=256, help="tokens per step (decode batch)")
+    ap.add_argument("--mask-bias", type=float, default=-1.04)
+    ap.add_argument("--sets", type=int, default=0, help="weight sets to rotate (0 = auto)")
+    ap.add_argument("--sweep", default="1,8,32,128,256",
+                    help="decode batch sizes for the sweep ('' to skip)")
+    ap.add_argument("--sweep-steps", type=int, default=100)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle sample")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+def algorithmic(n_act, P, T, d, E, I):
+    """Algorithmic HBM bytes and FLOPs of one layer call and of its stages.
+
+    Unit of work: one active expert (count >= 1) = 3*d*I bf16 weights read
+    once (2*d*I gate/up rows, d*I down rows); one active pair = 6*d*I FLOPs;
+    the router reads 2*E*d bf16 weights and does 4*d*E FLOPs per token.
+    """
+    b = 2  # bf16
+    up = n_act * 2 * I * d * b + T * d * b + P * I * b
+    down = n_act * d * I * b + P * I * b + P * d * b
+    layer = n_act * 3 * d * I * b + 2 * E * d * b + 2 * T * d * b
+    flops = 6.0 * d * I * P + 4.0 * d * E * T
+    return {"up": up, "down": down, "layer": layer, "flops": flops}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import dynamic_expert_sparsity_amd as B
+    from dynamic_expert_sparsity_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B.lib()
+
+    shape = synth.SHAPES["qwen3"]
+    d, E, K, I = shape.d, shape.E, shape.K, shape.I
+    sweep = [int(v) for v in args.sweep.split(",") if v.strip()] if args.sweep else []
+    T_max = max([args.T] + sweep)
+
+    # weight sets: enough that the bytes touched between two uses of one set
+    # exceed the 256 MB infinity cache by a wide margin
+    per_set_bytes = E * 3 * d * I * 2
+    if args.sets:
+        n_sets = args.sets
+    else:
+        n_sets = 4 if not sweep else 48
+    free, total = torch.cuda.mem_get_info()
+    n_sets = max(1, min(n_sets, int(0.6 * free // per_set_bytes)))
+    log(f"drawing {n_sets} weight sets ({n_sets * per_set_bytes / 1e9:.1f} GB) on {dev}")
+    t0 = time.time()
+    sets = [synth.make_layer(shape, T_max, seed=0, layer=s, mask_bias=args.mask_bias, device=dev)
+            for s in range(n_sets)]
+    zeros_mask = torch.zeros_like(sets[0]["W_mask"])
+    torch.cuda.synchronize()
+    log(f"drawn in {time.time() - t0:.1f}s")
+
+    stream = torch.cuda.current_stream()
+
+    def make_layers(T, allones=False, ns=n_sets):
+        Ls = []
+        for s in range(ns):
+            S = sets[s]
+            Ls.append((B.MoELayer(S["W_gate"], zeros_mask if allones else S["W_mask"], S["W_gu"],
+                                  S["W_dt"], K), S["x"][:T].contiguous()))
+        return Ls
+
+    def timed(Ls, steps, warmup, events=None):
+        """Time `steps` calls (wall clock, synchronised on both sides).
+
+        events=None: no events (the clean timing).  events="stages": one event
+        between every two stages (diagnostic: each record adds a few us).
+        events=<stage name>: two events bracketing that stage only, on the
+        launch stream, averaged over the steps (the kernel's launch duration).
+        Returns (ms per step, dict of per-stage ms per step or None)."""
+        ns = len(Ls)
+        for i in range(warmup):
+            lay, x = Ls[i % ns]
+            lay(x)
+        n_ev = len(B.STAGES) + 1
+        ev = B.HipEvents(n_ev * steps) if events else None
+        slots = None
+        if events and events != "stages":
+            j = B.STAGES.index(events)
+            slots = (j, j + 1)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            lay, x = Ls[i % ns]
+            if ev is None:
+                lay(x)
+            else:
+                hs = ev.handles[i * n_ev:(i + 1) * n_ev]
+                if slots:
+                    hs = [h if q in slots else None for q, h in enumerate(hs)]
+                lay(x, events=hs)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        stages = None
+        if ev is not None:
+            stages = {}
+            if slots:
+                stages[events] = sum(ev.elapsed_ms(i * n_ev + slots[0], i * n_ev + slots[1])
+                                     for i in range(steps)) / steps
+            else:
+                for j, name in enumerate(B.STAGES):
+                    stages[name] = sum(ev.elapsed_ms(i * n_ev + j, i * n_ev + j + 1)
+                                       for i in range(steps)) / steps
+                stages["gpu_total"] = sum(ev.elapsed_ms(i * n_ev, i * n_ev + n_ev - 1)
+                                          for i in range(steps)) / steps
+            ev.close()
+        return ms, stages
+
+    def counts(Ls):
+        """Active pairs and active experts per set (from the last call's routing)."""
+        out = []
+        for lay, x in Ls:
+            lay(x)
+            torch.cuda.synchronize()
+            na = lay.routing["num_active"].cpu().tolist()
+            out.append((na[0], na[2]))
+        return out
+
+    def measure(T, steps, warmup, allones=False, kernels=()):
+        ns = n_sets
+        Ls = make_layers(T, allones, ns)
+        ms, _ = timed(Ls, steps, warmup)
+        _, stages = timed(Ls, max(20, steps // 4), 5, events="stages")
+        kern = {k: timed(Ls, steps, 5, events=k)[1][k] for k in kernels}
+        cs = counts(Ls)
+        P = sum(c[0] for c in cs) / len(cs)
+        n_act = sum(c[1] for c in cs) / len(cs)
+        alg = algorithmic(n_act, P, T, d, E, I)
+        r = {"T": T, "ms_per_step": ms, "tok_per_s": T / (ms * 1e-3),
+             "active_pairs": P, "active_experts": n_act, "keep_rate": P / (T * K),
+             "layer_bytes": alg["layer"], "layer_GBps": alg["layer"] / (ms * 1e-3) / 1e9}
+        r["layer_hbm_frac"] = r["layer_GBps"] / HBM_PEAK_GBPS
+        r["stages_ms_evented"] = stages
+        r["kernel_ms"] = kern
+        r["_alg"] = alg
+        del Ls
+        return r
+
+    # ---- headline --------------------------------------------------------
+    log(f"headline: T={args.T}, {args.steps} steps after {args.warmup} warm-up")
+    head = measure(args.T, args.steps, args.warmup, kernels=("up", "down"))
+    ones = measure(args.T, args.steps, args.warmup, allones=True, kernels=("up", "down"))
+    km = head["kernel_ms"]
+    dom = max(km, key=km.get)
+    alg = head["_alg"]
+    achieved = alg[dom] / (km[dom] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": f"expert_{dom}", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": None, "alg_bytes_per_launch": alg[dom],
+                "avg_launch_ms": round(km[dom], 5),
+                "other": {k: {"avg_launch_ms": round(v, 5),
+                              "GBps": round(alg[k] / (v * 1e-3) / 1e9, 1)}
+                          for k, v in km.items() if k != dom}}
+
+    # ---- sweep -------------------------------------------------------------
+    sweep_out = []
+    for T in sweep:
+        m = measure(T, args.sweep_steps, 10)
+        o = measure(T, args.sweep_steps, 10, allones=True)
+        sweep_out.append({
+            "T": T,
+            "masked": {k: _r(v) for k, v in m.items() if not k.startswith("_")},
+            "allones": {k: _r(v) for k, v in o.items() if not k.startswith("_")},
+            "speedup_vs_allones": round(o["ms_per_step"] / m["ms_per_step"], 3),
+            "byte_ratio_allones": round(o["layer_bytes"] / m["layer_bytes"], 3),
+        })
+        log(f"sweep T={T}: masked {m['ms_per_step']*1e3:.1f} us, "
+            f"all-ones {o['ms_per_step']*1e3:.1f} us")
+
+    # ---- CPU baseline: the fp64 oracle on this host's cores ---------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(sets, args.T, K, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(head["tok_per_s"], 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": synth.workload_name("qwen3", args.T, mask_bias=args.mask_bias),
+                   "phase": "decode", "T": args.T, "d": d, "E": E, "K": K, "I": I,
+                   "mask_bias": args.mask_bias, "weight_sets": n_sets,
+                   "keep_rate": round(head["keep_rate"], 4),
+                   "active_experts": head["active_experts"], "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "layer_hbm": {"bytes": head["layer_bytes"], "GBps": round(head["layer_GBps"], 1),
+                      "frac": round(head["layer_hbm_frac"], 4)},
+        "stages_ms_evented": _r(head["stages_ms_evented"]),
+        "allones": {"ms_per_step": round(ones["ms_per_step"], 5),
+                    "tok_per_s": round(ones["tok_per_s"], 1),
+                    "active_experts": ones["active_experts"],
+                    "layer_bytes": ones["layer_bytes"],
+                    "kernel_ms": _r(ones["kernel_ms"]),
+                    "speedup_masked_vs_allones": round(ones["ms_per_step"] / head["ms_per_step"], 3)},
+        "sweep": sweep_out,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def _r(v):
+    if isinstance(v, float):
+        return round(v, 5)
+    if isinstance(v, dict):
+        return {k: _r(x) for k, x in v.items()}
+    return v
+
+
+def cpu_baseline(sets, T, K, budget_s):
+    """Time the fp64 oracle (route from scratch + Eq. 8) on this host."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        blas = None
+    cores = len(os.sched_getaffinity(0))
+    total_t = 0.0
+    total_tok = 0
+    calls = 0
+    for s, S in enumerate(sets):
+        x = S["x"][:T].float().cpu().numpy()
+        Wg = S["W_gate"].float().cpu().numpy()
+        Wm = S["W_mask"].float().cpu().numpy()
+        # host float32 copies of the experts this batch uses (not timed)
+        R0 = oracle.route(x, Wg, Wm, K)
+        used = sorted(set(int(e) for e in np.asarray(R0["masked_ids"]).ravel() if e >= 0))
+        Wgu = {e: S["W_gu"][e].float().cpu().numpy() for e in used}
+        Wdt = {e: S["W_dt"][e].float().cpu().numpy() for e in used}
+        t0 = time.perf_counter()
+        R = oracle.route(x, Wg, Wm, K)
+        oracle.forward(x, Wg, Wm, Wgu, Wdt, K, routing=R)
+        total_t += time.perf_counter() - t0
+        total_tok += T
+        calls += 1
+        del Wgu, Wdt
+        if total_t >= budget_s or calls >= 16:
+            break
+    log(f"cpu baseline: {calls} layer calls of T={T} in {total_t:.1f}s")
+    return {"value": round(total_tok / total_t, 2), "unit": "tok/s", "cores": cores,
+            "blas_threads": blas, "kind": "oracle",
+            "sample": f"{calls} layer calls x {T} tokens (distinct weight sets), fp64 route + Eq. 8, "
+                      f"{total_t:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

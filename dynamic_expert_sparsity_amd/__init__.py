@@ -18,7 +18,7 @@ __all__ = [
     "BEAM_OK", "BEAM_EINVAL", "BEAM_EUNSUPPORTED", "BEAM_EWORKSPACE", "BEAM_EHIP",
     "BEAM_F32", "BEAM_BF16", "BEAM_FORCE_DECODE", "BEAM_FORCE_PREFILL",
     "STAGES", "BeamError", "lib", "library_path", "Desc", "Routing", "Sizes",
-    "make_desc", "query", "alloc_routing", "route", "forward", "MoELayer",
+    "make_desc", "query", "alloc_routing", "route", "forward", "MoELayer", "HipEvents",
 ]
 
 BEAM_OK, BEAM_EINVAL, BEAM_EUNSUPPORTED, BEAM_EWORKSPACE, BEAM_EHIP = 0, -1, -2, -3, -4
@@ -73,6 +73,7 @@ def lib() -> ctypes.CDLL:
             raise ImportError(f"{path} is missing: build it with "
                               "`python -m dynamic_expert_sparsity_amd.build`")
         L = ctypes.CDLL(path)
+        _check_single_hip_runtime()
         vp, sz = ctypes.c_void_p, ctypes.c_size_t
         L.beam_moe_query.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Sizes)]
         L.beam_moe_query.restype = ctypes.c_int
@@ -93,6 +94,55 @@ def lib() -> ctypes.CDLL:
         L.beam_moe_version.restype = ctypes.c_char_p
         _lib = L
     return _lib
+
+
+def _hip_runtimes() -> set:
+    try:
+        with open("/proc/self/maps") as f:
+            return {l.split()[-1] for l in f if "libamdhip64" in l}
+    except OSError:
+        return set()
+
+
+def _check_single_hip_runtime():
+    # torch ships its own HIP runtime with the same SONAME; the library must
+    # bind to that one so torch's streams, events and allocations are valid in
+    # its calls.  Importing torch before loading the library guarantees it.
+    libs = _hip_runtimes()
+    if len(libs) > 1:
+        raise ImportError(f"two HIP runtimes are loaded ({sorted(libs)}); import torch before "
+                          "loading libbeam_moe.so")
+
+
+class HipEvents:
+    """A set of HIP events (timing only) created in the process's HIP runtime."""
+
+    def __init__(self, n: int):
+        lib()
+        self._hip = ctypes.CDLL("libamdhip64.so.7")
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                  ctypes.c_void_p]
+        self._hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.handles = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            if self._hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.handles.append(h.value)
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        self._hip.hipEventSynchronize(self.handles[j])
+        ms = ctypes.c_float()
+        if self._hip.hipEventElapsedTime(ctypes.byref(ms), self.handles[i], self.handles[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def close(self):
+        for h in self.handles:
+            self._hip.hipEventDestroy(h)
+        self.handles = []
 
 
 def _check(status: int):
@@ -219,7 +269,7 @@ def route(x, W_gate, W_mask, K, block_m=0, flags=0, tau=0.0, stream=None) -> dic
     _gpu_tensor("W_gate", W_gate, x.dtype, (E, d))
     _gpu_tensor("W_mask", W_mask, x.dtype, (E, d))
     T = x.shape[0]
-    desc = make_desc(T, d, E, K, 32, x.dtype, block_m, flags, tau)
+    desc = make_desc(T, d, E, K, 64, x.dtype, block_m, flags, tau)  # I unused by routing
     sizes = query(desc)
     R = alloc_routing(desc, sizes, x.device)
     ws = torch.empty(max(sizes["route_workspace_bytes"], 256), dtype=torch.uint8, device=x.device)

@@ -53,10 +53,10 @@ int make_plan(const beam_moe_desc *desc, Plan &p) {
         return fail(BEAM_EINVAL, "reserved fields must be 0");
 
     if (D.E > 256) return fail(BEAM_EUNSUPPORTED, "E=%d > 256", D.E);
-    if (D.K > 64) return fail(BEAM_EUNSUPPORTED, "K=%d > 64", D.K);
-    if (D.dtype == BEAM_BF16 && (D.d % 128 != 0 || D.I % 32 != 0))
-        return fail(BEAM_EUNSUPPORTED, "bf16 layer needs d %% 128 == 0 and I %% 32 == 0 (d=%d I=%d)",
-                    D.d, D.I);
+    if (D.K > 16) return fail(BEAM_EUNSUPPORTED, "K=%d > 16", D.K);
+    if (D.dtype == BEAM_BF16 && (D.d % 128 != 0 || D.I % 64 != 0 || D.I > 2040))
+        return fail(BEAM_EUNSUPPORTED,
+                    "bf16 layer needs d %% 128 == 0, I %% 64 == 0 and I <= 2040 (d=%d I=%d)", D.d, D.I);
     if (D.flags & BEAM_FORCE_PREFILL)
         return fail(BEAM_EUNSUPPORTED, "the tiled prefill path is not available in this build");
     const long long TK = (long long)D.T * D.K;
@@ -70,25 +70,10 @@ int make_plan(const beam_moe_desc *desc, Plan &p) {
     // m = [sigmoid(z) >= tau]  <=>  z >= ln(tau / (1 - tau)); exactly 0 at tau = 0.5
     p.thr = tau == 0.5f ? 0.f : (float)std::log((double)tau / (1.0 - (double)tau));
 
-    // router logits: token tile, and splits of d so that small T still
-    // spreads the 2*E*d weight read over many workgroups
-    p.r_tt = D.T <= 64 ? 16 : 64;
-    if (p.dtype == BEAM_BF16) {
-        const long long tiles = (long long)((D.T + p.r_tt - 1) / p.r_tt) * ((2 * D.E + 63) / 64);
-        long long splits = 1024 / (tiles > 0 ? tiles : 1);
-        const long long max_splits = D.d / 128;
-        if (splits > max_splits) splits = max_splits;
-        if (splits < 1) splits = 1;
-        int dchunk = (int)((D.d + splits - 1) / splits);
-        dchunk = (dchunk + 31) / 32 * 32;
-        p.r_dchunk = dchunk;
-        p.r_splits = (D.d + dchunk - 1) / dchunk;
-    } else {
-        p.r_splits = 1;
-        p.r_dchunk = D.d;
-    }
     p.s_ts = 64;
     p.n_tiles = (D.T + 63) / 64;
+    p.small_route = D.T <= 256;
+    p.fuse_scatter = !p.small_route && p.n_tiles <= 16;
     p.max_active = (int)(TK < D.E ? TK : D.E);
     const long long cap_raw = TK + (long long)p.max_active * (p.bm - 1);
     p.cap = (cap_raw + p.bm - 1) / p.bm * p.bm;
@@ -96,10 +81,11 @@ int make_plan(const beam_moe_desc *desc, Plan &p) {
 
     const size_t elt = p.dtype == BEAM_BF16 ? 2 : 4;
     size_t off = 0;
-    p.off_partial = off;   off = align_up(off + (size_t)p.r_splits * D.T * 2 * D.E * 4, 256);
     p.off_tile_mask = off; off = align_up(off + (size_t)p.n_tiles * D.E * 8, 256);
     p.off_tile_base = off; off = align_up(off + (size_t)p.n_tiles * D.E * 4, 256);
     p.off_pair_pos = off;  off = align_up(off + (size_t)TK * 4, 256);
+    p.off_meta = off;      off = align_up(off + (size_t)D.E * 16, 256);
+    p.off_stok = off;      off = align_up(off + (size_t)p.cap * 4, 256);
     p.route_bytes = off;
     p.off_h = off;         off = align_up(off + (size_t)p.cap * D.I * elt, 256);
     p.off_o = off;         off = align_up(off + (size_t)p.cap * D.d * elt, 256);
@@ -130,10 +116,11 @@ int check_routing(const beam_moe_routing *o, Routing &r) {
 Work carve(const Plan &p, void *ws) {
     char *b = static_cast<char *>(ws);
     Work w;
-    w.partial = reinterpret_cast<float *>(b + p.off_partial);
     w.tile_mask = reinterpret_cast<uint64_t *>(b + p.off_tile_mask);
     w.tile_base = reinterpret_cast<int32_t *>(b + p.off_tile_base);
     w.pair_pos = reinterpret_cast<int32_t *>(b + p.off_pair_pos);
+    w.meta = reinterpret_cast<int32_t *>(b + p.off_meta);
+    w.sorted_tok = reinterpret_cast<int32_t *>(b + p.off_stok);
     w.h = b + p.off_h;
     w.o = b + p.off_o;
     return w;
@@ -142,7 +129,7 @@ Work carve(const Plan &p, void *ws) {
 struct Events {
     hipEvent_t *ev;
     hipStream_t s;
-    hipError_t mark(int i) const { return ev ? hipEventRecord(ev[i], s) : hipSuccess; }
+    hipError_t mark(int i) const { return ev && ev[i] ? hipEventRecord(ev[i], s) : hipSuccess; }
 };
 
 #define BEAM_TRY(expr, stage)                                                             \
@@ -155,13 +142,13 @@ struct Events {
 int enqueue_route(const Plan &p, const void *x, const void *Wg, const void *Wm, const Routing &r,
                   const Work &w, hipStream_t s, const Events &ev) {
     BEAM_TRY(ev.mark(BEAM_STAGE_ROUTER), "event");
-    BEAM_TRY(launch_router_logits(p, x, Wg, Wm, w, s), "router logits");
+    BEAM_TRY(launch_router_logits(p, x, Wg, Wm, r, s), "router logits");
     BEAM_TRY(ev.mark(BEAM_STAGE_SELECT), "event");
     BEAM_TRY(launch_select(p, r, w, s), "select");
     BEAM_TRY(ev.mark(BEAM_STAGE_SCAN), "event");
-    BEAM_TRY(launch_scan(p, r, w, s), "compaction scan");
+    if (!p.small_route) BEAM_TRY(launch_scan(p, r, w, s), "compaction scan");
     BEAM_TRY(ev.mark(BEAM_STAGE_SCATTER), "event");
-    BEAM_TRY(launch_scatter(p, r, w, s), "compaction scatter");
+    if (!p.small_route) BEAM_TRY(launch_scatter(p, r, w, s), "compaction scatter");
     return BEAM_OK;
 }
 
@@ -223,9 +210,6 @@ int beam_moe_forward_ex(const beam_moe_desc *desc, const void *x, const void *W_
     if (!aligned(ws, 16)) return fail(BEAM_EINVAL, "workspace is NULL or not 16-byte aligned");
     if (ws_bytes < p.total_bytes)
         return fail(BEAM_EWORKSPACE, "workspace has %zu bytes, forward needs %zu", ws_bytes, p.total_bytes);
-    if (stage_events)
-        for (int i = 0; i <= BEAM_NUM_STAGES; ++i)
-            if (!stage_events[i]) return fail(BEAM_EINVAL, "stage_events[%d] is NULL", i);
 
     const Work w = carve(p, ws);
     const Events ev{stage_events, stream};

@@ -50,6 +50,15 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const u32x4 &a, const u32x4 &b, f3
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// 16-byte scalar load of a workgroup-uniform address (one s_load_dwordx4,
+// completed inside the asm block).
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 sload16(const void *p) {
+    i32x4 v;
+    asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+    return v;
+}
+
 __device__ __forceinline__ u32x4 ld16(const void *p) {
     return *reinterpret_cast<const u32x4 *>(p);
 }

@@ -1,7 +1,7 @@
-// a4: grouping of the active (token, expert) pairs.  Masked slots (id -1)
-// are left out of the per-expert counts, so masked pairs are never scheduled
-// (news article on the BEAM paper, section 5, the modified expert/token
-// grouping kernel).
+// a4: grouping of the active (token, expert) pairs into per-expert lists.
+// Masked slots (id -1) are left out of the per-expert counts, so masked pairs
+// are never scheduled (news article on the BEAM paper, section 5, the
+// modified expert/token grouping kernel).
 //
 // Input: per select tile (64 tokens) and expert, the 64-bit set of tile
 // tokens that have an active pair for that expert (built by the select
@@ -11,27 +11,36 @@
 // so a pair's position in its expert's list is
 //   offsets[e] + (pairs of e in earlier tiles) + rank,
 // which lists each expert's pairs in ascending pair id with no atomics.
-#include "common.h"
-#include "kernels.h"
+#include "compact_dev.h"
 
 namespace beam {
 
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(v, off);
-        if (lane >= off) v += y;
+__device__ __forceinline__ void scatter_pair(int p, int K, int E, const Routing &r,
+                                             const int *off, const int32_t *tile_base,
+                                             const uint64_t *tile_mask, int32_t *pair_pos,
+                                             int32_t *sorted_tok) {
+    const int e = r.masked_ids[p];
+    if (e < 0) {
+        pair_pos[p] = -1;
+        return;
     }
-    return v;
+    const int t = p / K;
+    const size_t q = (size_t)(t >> 6) * E + e;
+    const int rank = __popcll(tile_mask[q] & ((1ull << (t & 63)) - 1ull));
+    place_pair(p, e, off[e] + tile_base[q] + rank, K, r, pair_pos, sorted_tok);
 }
 
 // One workgroup of 1024 threads.  Thread (g, e) with g = tid / E sums the
-// popcounts of a contiguous range of tiles for expert e; group partials are
-// scanned to give every (tile, expert) its base, then wave 0 scans the
-// experts (4 per lane, E <= 256) into block-padded offsets.
+// popcounts of a contiguous range of tiles for expert e; group partials give
+// every (tile, expert) its base; wave 0 scans the experts into block-padded
+// offsets.  With fuse_scatter the same workgroup then places every pair.
 __global__ __launch_bounds__(1024) void compact_scan(const uint64_t *__restrict__ tile_mask,
-                                                     int n_tiles, int E, int bm, int TK,
-                                                     Routing r, int32_t *__restrict__ tile_base) {
+                                                     int n_tiles, int E, int bm, int K, int TK,
+                                                     Routing r, int32_t *__restrict__ tile_base,
+                                                     int32_t *__restrict__ pair_pos,
+                                                     int32_t *__restrict__ meta,
+                                                     int32_t *__restrict__ sorted_tok,
+                                                     int fuse_scatter) {
     __shared__ int s_part[1024];
     __shared__ int s_cnt[256];
     __shared__ int s_off[257];
@@ -61,102 +70,40 @@ __global__ __launch_bounds__(1024) void compact_scan(const uint64_t *__restrict_
             tile_base[(size_t)t * E + e] = base;
             base += __popcll(tile_mask[(size_t)t * E + e]);
         }
-        if (g == 0) {
-            s_cnt[e] = total;
-            r.expert_counts[e] = total;
-        }
+        if (g == 0) s_cnt[e] = total;
     }
     __syncthreads();
-
-    if (tid < 64) {
-        const int lane = tid;
-        int c[4], pad[4], act[4];
-        int sc = 0, sp = 0, sa = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int ex = lane * 4 + j;
-            c[j] = ex < E ? s_cnt[ex] : 0;
-            pad[j] = (c[j] + bm - 1) / bm * bm;
-            act[j] = c[j] > 0 ? 1 : 0;
-            sc += c[j];
-            sp += pad[j];
-            sa += act[j];
-        }
-        const int ic = wave_incl_scan(sc, lane);
-        const int ip = wave_incl_scan(sp, lane);
-        const int ia = wave_incl_scan(sa, lane);
-        int op = ip - sp, oa = ia - sa;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int ex = lane * 4 + j;
-            if (ex < E) {
-                s_off[ex] = op;
-                r.expert_offsets[ex] = op;
-                if (act[j]) r.active_experts[oa] = ex;
-            }
-            op += pad[j];
-            oa += act[j];
-        }
-        if (lane == 63) {
-            s_off[E] = ip;
-            r.expert_offsets[E] = ip;
-            r.num_active[0] = ic;
-            r.num_active[1] = ip;
-            r.num_active[2] = ia;
-            r.num_active[3] = ip / bm;
-        }
-    }
+    if (tid < 64) offsets_from_counts(s_cnt, s_off, E, bm, r, meta, tid);
     __syncthreads();
-
-    // block -> expert map and pad entries, one thread per block of bm slots
-    const int n_blocks = s_off[E] / bm;
-    for (int b = tid; b < n_blocks; b += 1024) {
-        const int pos = b * bm;
-        int lo = 0, hi = E - 1;  // last expert with s_off[ex] <= pos
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (s_off[mid] <= pos) lo = mid; else hi = mid - 1;
-        }
-        // skip experts with empty segments that share the same offset
-        while (lo + 1 < E && s_off[lo + 1] <= pos) ++lo;
-        r.block_expert[b] = lo;
-        const int end_valid = s_off[lo] + s_cnt[lo];
-        for (int q = max(pos, end_valid); q < pos + bm; ++q) r.sorted_pairs[q] = TK;
-    }
+    blocks_and_pads(s_off, s_cnt, E, bm, TK, r, tid, 1024);
+    if (fuse_scatter)
+        for (int p = tid; p < TK; p += 1024)
+            scatter_pair(p, K, E, r, s_off, tile_base, tile_mask, pair_pos, sorted_tok);
 }
 
-__global__ __launch_bounds__(256) void compact_scatter(
-    const int32_t *__restrict__ masked_ids, const int32_t *__restrict__ offsets,
-    const int32_t *__restrict__ tile_base, const uint64_t *__restrict__ tile_mask, int TK,
-    int K, int E, int32_t *__restrict__ sorted_pairs, int32_t *__restrict__ pair_pos) {
+__global__ __launch_bounds__(256) void compact_scatter(Routing r,
+                                                      const int32_t *__restrict__ tile_base,
+                                                      const uint64_t *__restrict__ tile_mask,
+                                                      int TK, int K, int E,
+                                                      int32_t *__restrict__ pair_pos,
+                                                      int32_t *__restrict__ sorted_tok) {
     const int p = blockIdx.x * 256 + threadIdx.x;
     if (p >= TK) return;
-    const int e = masked_ids[p];
-    if (e < 0) {
-        pair_pos[p] = -1;
-        return;
-    }
-    const int t = p / K;
-    const int tile = t >> 6;
-    const int tl = t & 63;
-    const size_t q = (size_t)tile * E + e;
-    const int rank = __popcll(tile_mask[q] & ((1ull << tl) - 1ull));
-    const int pos = offsets[e] + tile_base[q] + rank;
-    sorted_pairs[pos] = p;
-    pair_pos[p] = pos;
+    scatter_pair(p, K, E, r, r.expert_offsets, tile_base, tile_mask, pair_pos, sorted_tok);
 }
 
 hipError_t launch_scan(const Plan &p, const Routing &r, const Work &w, hipStream_t s) {
-    compact_scan<<<1, 1024, 0, s>>>(w.tile_mask, p.n_tiles, p.E, p.bm, p.T * p.K, r,
-                                    w.tile_base);
+    compact_scan<<<1, 1024, 0, s>>>(w.tile_mask, p.n_tiles, p.E, p.bm, p.K, p.T * p.K, r,
+                                    w.tile_base, w.pair_pos, w.meta, w.sorted_tok,
+                                    p.fuse_scatter);
     return hipGetLastError();
 }
 
 hipError_t launch_scatter(const Plan &p, const Routing &r, const Work &w, hipStream_t s) {
+    if (p.fuse_scatter) return hipSuccess;
     const int TK = p.T * p.K;
-    compact_scatter<<<(TK + 255) / 256, 256, 0, s>>>(r.masked_ids, r.expert_offsets,
-                                                     w.tile_base, w.tile_mask, TK, p.K, p.E,
-                                                     r.sorted_pairs, w.pair_pos);
+    compact_scatter<<<(TK + 255) / 256, 256, 0, s>>>(r, w.tile_base, w.tile_mask, TK, p.K, p.E,
+                                                     w.pair_pos, w.sorted_tok);
     return hipGetLastError();
 }
 

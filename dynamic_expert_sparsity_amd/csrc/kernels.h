@@ -13,18 +13,16 @@ struct Plan {
     int bm;             // block_m
     int path;           // 0 streaming (decode), 1 tiled (prefill)
     float thr;          // mask logit threshold: m = [z >= thr]
-    // router logits
-    int r_tt;           // tokens per router tile (multiple of 16)
-    int r_splits;       // splits of d (partial sums reduced in fixed order)
-    int r_dchunk;       // d per split (multiple of 32)
     // select / compaction
     int s_ts;           // tokens per select tile (64)
     int n_tiles;        // ceil(T / s_ts)
+    int small_route;    // T <= 256: select + compaction in one workgroup
+    int fuse_scatter;   // few tiles: the scan workgroup also places the pairs
     long long cap;          // sorted_pairs capacity
     long long n_blocks_cap; // block_expert capacity
     int max_active;     // host upper bound on experts with >= 1 active pair
     // workspace carve-up (byte offsets) and totals
-    size_t off_partial, off_tile_mask, off_tile_base, off_pair_pos, off_h, off_o;
+    size_t off_tile_mask, off_tile_base, off_pair_pos, off_meta, off_stok, off_h, off_o;
     size_t route_bytes, total_bytes;
 };
 
@@ -40,16 +38,17 @@ struct Routing {
 };
 
 struct Work {  // workspace views
-    float *partial;
     uint64_t *tile_mask;
     int32_t *tile_base;
-    int32_t *pair_pos;
+    int32_t *pair_pos;   // [T*K] sorted position of each pair, -1 if masked
+    int32_t *meta;       // [E][4] per active expert: {expert, offset, count, 0}
+    int32_t *sorted_tok; // [cap] token of each sorted position (pads: unset)
     void *h;
     void *o;
 };
 
 hipError_t launch_router_logits(const Plan &p, const void *x, const void *Wg, const void *Wm,
-                                const Work &w, hipStream_t s);
+                                const Routing &r, hipStream_t s);
 hipError_t launch_select(const Plan &p, const Routing &r, const Work &w, hipStream_t s);
 hipError_t launch_scan(const Plan &p, const Routing &r, const Work &w, hipStream_t s);
 hipError_t launch_scatter(const Plan &p, const Routing &r, const Work &w, hipStream_t s);

@@ -5,32 +5,35 @@
 // Eq. 5 (z = x W_m), Eq. 6 (m = [sigmoid(z) >= 0.5], evaluated as z >= 0),
 // Eq. 7 (g_hat = g * m, no renormalisation).  Masked slots get the expert id
 // -1 (news article on the paper, section 5, the modified routing kernel).
-#include "common.h"
-#include "kernels.h"
+#include "compact_dev.h"
 
 namespace beam {
 
 // ---------------------------------------------------------------------------
 // Router logits, bf16, MFMA 16x16x32.  The two routers are one GEMM with
 // 2E output columns: column n < E is W_gate row n, column E + n is W_mask
-// row n.  Grid: (token tiles of 16*MT, column tiles of 64, splits of d).
-// Each wave owns 16 columns; A (x rows) and B (weight rows) are both
-// k-contiguous, so every lane's 16-byte load lands directly in MFMA layout.
-// Out-of-range tokens / columns load a clamped row and their results are
-// not stored.  partial[s][t][n] holds the split-s partial sums.
+// row n.  A workgroup owns 16 columns and 16*MT tokens; its NW waves split d
+// (every wave requests all of its x and weight fragments before the first
+// MFMA) and their partial sums meet in LDS, where wave 0 adds them in wave
+// order and writes the finished float32 logits.  A (x rows) and B (weight
+// rows) are both k-contiguous, so every lane's 16-byte load lands directly
+// in MFMA layout.  Out-of-range tokens / columns load a clamped row and their
+// results are not stored.
 // ---------------------------------------------------------------------------
-template <int MT>
-__global__ __launch_bounds__(256) void router_logits_bf16(
+template <int MT, int NW>
+__global__ __launch_bounds__(NW * 64) void router_logits_bf16(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ Wg,
-    const bf16_t *__restrict__ Wm, float *__restrict__ partial, int T, int d, int E,
-    int dchunk) {
+    const bf16_t *__restrict__ Wm, float *__restrict__ gate_logits,
+    float *__restrict__ mask_logits, int T, int d, int E) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int twoE = 2 * E;
-    const int n = blockIdx.y * 64 + wave * 16 + (lane & 15);
+    const int n = blockIdx.y * 16 + (lane & 15);
     const int nc = n < twoE ? n : twoE - 1;
-    const bf16_t *brow = nc < E ? Wg + (size_t)nc * d : Wm + (size_t)(nc - E) * d;
     const int kq = (lane >> 4) * 8;
+    const int dq = d / NW;
+    const int kb = wave * dq + kq;
+    const bf16_t *brow = (nc < E ? Wg + (size_t)nc * d : Wm + (size_t)(nc - E) * d) + kb;
     const int tbase = blockIdx.x * 16 * MT;
 
     const bf16_t *arow[MT];
@@ -38,31 +41,48 @@ __global__ __launch_bounds__(256) void router_logits_bf16(
     for (int m = 0; m < MT; ++m) {
         int t = tbase + m * 16 + (lane & 15);
         t = t < T ? t : T - 1;
-        arow[m] = x + (size_t)t * d + kq;
+        arow[m] = x + (size_t)t * d + kb;
     }
-    brow += kq;
-
     f32x4 acc[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int k0 = blockIdx.z * dchunk;
-    const int k1 = min(d, k0 + dchunk);
-#pragma unroll 4
-    for (int k = k0; k < k1; k += 32) {
-        const u32x4 b = ld16(brow + k);
+    constexpr int CH = 8;  // k-steps requested per batch
+    for (int k0 = 0; k0 < dq; k0 += 32 * CH) {
+        u32x4 b[CH], a[CH][MT];
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int m = 0; m < MT; ++m) acc[m] = mfma16x16x32(ld16(arow[m] + k), b, acc[m]);
+        for (int c = 0; c < CH; ++c) {
+            const int k = k0 + 32 * c;
+            if (k < dq) {
+                b[c] = ld16(brow + k);
+#pragma unroll
+                for (int m = 0; m < MT; ++m) a[c][m] = ld16(arow[m] + k);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+            if (k0 + 32 * c < dq)
+#pragma unroll
+                for (int m = 0; m < MT; ++m) acc[m] = mfma16x16x32(a[c][m], b[c], acc[m]);
     }
 
-    if (n >= twoE) return;
-    float *out = partial + (size_t)blockIdx.z * T * twoE + n;
+    __shared__ f32x4 red[NW][MT][64];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) red[wave][m][lane] = acc[m];
+    __syncthreads();
+    if (wave != 0 || n >= twoE) return;
+    float *out = n < E ? gate_logits + n : mask_logits + (n - E);
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
+        f32x4 v = red[0][m][lane];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) v += red[w][m][lane];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = tbase + m * 16 + (lane >> 4) * 4 + i;
-            if (t < T) out[(size_t)t * twoE] = acc[m][i];
+            if (t < T) out[(size_t)t * E] = v[i];
         }
     }
 }
@@ -72,7 +92,7 @@ __global__ __launch_bounds__(256) void router_logits_bf16(
 template <typename T_>
 __global__ __launch_bounds__(256) void router_logits_generic(
     const T_ *__restrict__ x, const T_ *__restrict__ Wg, const T_ *__restrict__ Wm,
-    float *__restrict__ partial, int T, int d, int E) {
+    float *__restrict__ gate_logits, float *__restrict__ mask_logits, int T, int d, int E) {
     const int twoE = 2 * E;
     const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (long long)T * twoE) return;
@@ -82,137 +102,286 @@ __global__ __launch_bounds__(256) void router_logits_generic(
     const T_ *xr = x + (size_t)t * d;
     float acc = 0.f;
     for (int k = 0; k < d; ++k) acc = fmaf(elem<T_>::load(xr + k), elem<T_>::load(w + k), acc);
-    partial[idx] = acc;
+    if (n < E) gate_logits[(size_t)t * E + n] = acc;
+    else mask_logits[(size_t)t * E + (n - E)] = acc;
 }
 
 // ---------------------------------------------------------------------------
-// Select: one wavefront per token, a workgroup per tile of `TS` (= 64) tokens.
-// Lane l holds the logits of experts l, l+64, l+128, l+192.  K rounds of a
-// wave-wide arg-max under the key (value desc, expert asc) give the Top-K
-// slots in order; lane k keeps slot k.  Also builds, per tile and expert, the
-// 64-bit set of tile tokens with an active pair for that expert; the
-// compaction turns these into counts and stable ranks with popcounts.
+// Select (Eq. 4-7 per token).  A token is handled by LPT lanes of one
+// wavefront (LPT = 4 or 16, a DPP quad or row); lane i of the group holds the
+// gate logits of experts i*EJ .. i*EJ+EJ-1, so a wavefront handles 64/LPT
+// consecutive tokens.  K rounds of a group-wide arg-max under the key
+// (value desc, expert asc) give the Top-K slots in order (Eq. 4); slot k is
+// kept by lane k % LPT.  Softmax over the kept logits shifted by the largest
+// (Eq. 4); the winners' mask logits are gathered afterwards and m = z >= thr
+// (Eq. 6, thr = 0 for tau = 0.5); g_hat = g * m (Eq. 7); id -1 where masked.
+// tmask[e] collects, per 64-token tile, the set of tile tokens with an active
+// pair for expert e; s_mid (optional, LDS) receives the masked ids.
+//
+// The group reductions use DPP lane moves: swap neighbours, swap pairs (a
+// quad), then mirror within 8 and within 16 (a row).  Each step combines two
+// values that are the same pair for both partners, so every lane of the
+// group ends with the same result (also for the float sum).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ bool beats(float v, int e, float bv, int be) {
     return v > bv || (v == bv && e < be);
 }
 
-__global__ __launch_bounds__(256) void select_topk_mask(
-    const float *__restrict__ partial, int splits, int T, int E, int K, float thr,
-    Routing r, uint64_t *__restrict__ tile_mask) {
-    __shared__ unsigned long long tmask[256];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    for (int e = tid; e < E; e += 256) tmask[e] = 0ull;
-    __syncthreads();
+constexpr int DPP_QUAD_1032 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_2301 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_MIRROR = 0x140;
 
-    const int twoE = 2 * E;
-    const int t0 = blockIdx.x * 64;
-    for (int tl = wave; tl < 64; tl += 4) {
-        const int t = t0 + tl;
-        if (t >= T) break;
-        float rv[4], zv[4];
-        bool live[4];
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
+}
+
+constexpr int NO_EXPERT = 0x7fffffff;
+
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float &bv, int &be) {
+    const float ov = dpp_f<CTRL>(bv);
+    const int oe = dpp_i<CTRL>(be);
+    if (oe != NO_EXPERT && (be == NO_EXPERT || beats(ov, oe, bv, be))) {
+        bv = ov;
+        be = oe;
+    }
+}
+
+template <int LPT>
+__device__ __forceinline__ void group_argmax(float &bv, int &be) {
+    argmax_step<DPP_QUAD_1032>(bv, be);
+    argmax_step<DPP_QUAD_2301>(bv, be);
+    if constexpr (LPT == 16) {
+        argmax_step<DPP_ROW_HALF_MIRROR>(bv, be);
+        argmax_step<DPP_ROW_MIRROR>(bv, be);
+    }
+}
+
+template <int LPT>
+__device__ __forceinline__ float group_sum(float v) {
+    v += dpp_f<DPP_QUAD_1032>(v);
+    v += dpp_f<DPP_QUAD_2301>(v);
+    if constexpr (LPT == 16) {
+        v += dpp_f<DPP_ROW_HALF_MIRROR>(v);
+        v += dpp_f<DPP_ROW_MIRROR>(v);
+    }
+    return v;
+}
+
+// One wavefront: tokens t_first .. t_first + 64/LPT - 1 (all in one tile).
+template <int EJ, int LPT>
+__device__ __forceinline__ void select_group(int T, int E, int K, float thr, const Routing &r,
+                                             unsigned long long *tmask, int *s_mid, int t_first,
+                                             int lane) {
+    constexpr int SPL = 16 / LPT;  // slots kept per lane (K <= 16)
+    const int i = lane % LPT;
+    const int t = t_first + lane / LPT;
+    const bool valid = t < T;
+    const int tc = valid ? t : T - 1;
+    const int tl = t & 63;
+    const int e0 = i * EJ;
+    // 16-byte loads when every lane's run of EJ logits is 16-byte aligned and whole
+    const bool vec = (EJ % 4 == 0) && (E % 4 == 0) && (e0 + EJ <= E);
+    const float *gr = r.gate_logits + (size_t)tc * E + e0;
+
+    float rv[EJ];
+    if (vec) {
+        if constexpr (EJ % 4 == 0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int e = lane + 64 * j;
-            live[j] = e < E;
-            rv[j] = 0.f;
-            zv[j] = 0.f;
-            if (live[j]) {
-                for (int s = 0; s < splits; ++s) {
-                    const float *ps = partial + ((size_t)s * T + t) * twoE;
-                    rv[j] += ps[e];
-                    zv[j] += ps[E + e];
-                }
-                r.gate_logits[(size_t)t * E + e] = rv[j];
-                r.mask_logits[(size_t)t * E + e] = zv[j];
+            for (int j = 0; j < EJ / 4; ++j) {
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(gr + 4 * j);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) rv[4 * j + u] = a[u];
             }
         }
+    } else {
+#pragma unroll
+        for (int j = 0; j < EJ; ++j) rv[j] = e0 + j < E ? gr[j] : 0.f;
+    }
+    uint64_t live = 0;
+#pragma unroll
+    for (int j = 0; j < EJ; ++j)
+        if (e0 + j < E) live |= 1ull << j;
 
-        float v0 = 0.f, myv = 0.f;
-        int mye = 0;
-        for (int k = 0; k < K; ++k) {
-            float bv = 0.f;
-            int be = 0x7fffffff;
+    float v0 = 0.f, myv[SPL];
+    int mye[SPL];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int e = lane + 64 * j;
-                if (live[j] && (be == 0x7fffffff || rv[j] > bv)) {  // e ascending in j
-                    bv = rv[j];
-                    be = e;
-                }
-            }
+    for (int q = 0; q < SPL; ++q) {
+        myv[q] = 0.f;
+        mye[q] = 0;
+    }
+    for (int k = 0; k < K; ++k) {
+        float bv = 0.f;
+        int be = NO_EXPERT;
 #pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) {
-                const float ov = __shfl_xor(bv, off);
-                const int oe = __shfl_xor(be, off);
-                if (oe != 0x7fffffff && (be == 0x7fffffff || beats(ov, oe, bv, be))) {
-                    bv = ov;
-                    be = oe;
-                }
-            }
-            if ((be & 63) == lane) live[be >> 6] = false;
-            if (k == 0) v0 = bv;
-            if (lane == k) {
-                myv = bv;
-                mye = be;
+        for (int j = 0; j < EJ; ++j) {  // expert index ascends with j: ties keep the first
+            if (((live >> j) & 1ull) && (be == NO_EXPERT || rv[j] > bv)) {
+                bv = rv[j];
+                be = e0 + j;
             }
         }
-
-        // Softmax over the K kept logits, shifted by the largest one.
-        const float num = lane < K ? expf(myv - v0) : 0.f;
-        float den = num;
+        group_argmax<LPT>(bv, be);
+        const int jw = be - e0;
+        if (jw >= 0 && jw < EJ) live &= ~(1ull << jw);
+        if (k == 0) v0 = bv;
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
+        for (int q = 0; q < SPL; ++q)
+            if (k == i + LPT * q) {
+                myv[q] = bv;
+                mye[q] = be;
+            }
+    }
 
-        // z of this lane's slot expert lives in lane (mye & 63), register mye >> 6.
-        float zk = 0.f;
+    float num[SPL], part = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float zz = __shfl(zv[j], mye & 63);
-            if ((mye >> 6) == j) zk = zz;
-        }
-        if (lane < K) {
-            const float g = num / den;
-            const bool m = zk >= thr;
-            const size_t q = (size_t)t * K + lane;
-            r.topk_ids[q] = mye;
-            r.topk_weights[q] = g;
-            r.mask[q] = m ? 1 : 0;
-            r.g_hat[q] = m ? g : 0.f;
-            r.masked_ids[q] = m ? mye : -1;
-            if (m) atomicOr(&tmask[mye], 1ull << tl);
+    for (int q = 0; q < SPL; ++q) {
+        num[q] = i + LPT * q < K ? expf(myv[q] - v0) : 0.f;
+        part += num[q];
+    }
+    const float den = group_sum<LPT>(part);
+    if (!valid) return;
+#pragma unroll
+    for (int q = 0; q < SPL; ++q) {
+        const int k = i + LPT * q;
+        if (k < K) {
+            const float z = r.mask_logits[(size_t)t * E + mye[q]];
+            const float g = num[q] / den;
+            const bool m = z >= thr;
+            const int o = t * K + k;
+            r.topk_ids[o] = mye[q];
+            r.topk_weights[o] = g;
+            r.mask[o] = m ? 1 : 0;
+            r.g_hat[o] = m ? g : 0.f;
+            r.masked_ids[o] = m ? mye[q] : -1;
+            if (s_mid) s_mid[o] = m ? mye[q] : -1;
+            if (m) atomicOr(&tmask[mye[q]], 1ull << tl);
         }
     }
+}
+
+// One workgroup per 64-token tile: LPT waves of 64/LPT tokens each.
+template <int EJ, int LPT>
+__global__ __launch_bounds__(LPT * 64) void select_topk_mask(int T, int E, int K, float thr,
+                                                             Routing r,
+                                                             uint64_t *__restrict__ tile_mask) {
+    __shared__ unsigned long long tmask[256];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += LPT * 64) tmask[e] = 0ull;
     __syncthreads();
-    for (int e = tid; e < E; e += 256) tile_mask[(size_t)blockIdx.x * E + e] = tmask[e];
+    const int t_first = blockIdx.x * 64 + (tid >> 6) * (64 / LPT);
+    if (t_first < T) select_group<EJ, LPT>(T, E, K, thr, r, tmask, nullptr, t_first, tid & 63);
+    __syncthreads();
+    for (int e = tid; e < E; e += LPT * 64) tile_mask[(size_t)blockIdx.x * E + e] = tmask[e];
+}
+
+// T <= 256 (at most 4 tiles): select, counts, offsets, lists and pair
+// positions in one workgroup of 1024 threads; the tile sets and the masked
+// ids stay in LDS.
+constexpr int SMALL_TILES = 4;
+
+template <int EJ, int LPT>
+__global__ __launch_bounds__(1024) void route_small(int T, int E, int K, float thr, int bm,
+                                                    Routing r, int32_t *__restrict__ pair_pos,
+                                                    int32_t *__restrict__ meta,
+                                                    int32_t *__restrict__ sorted_tok) {
+    __shared__ unsigned long long tmask[SMALL_TILES][256];
+    __shared__ int s_mid[SMALL_TILES * 64 * 16];
+    __shared__ int s_base[SMALL_TILES][256];
+    __shared__ int s_cnt[256];
+    __shared__ int s_off[257];
+    constexpr int TPW = 64 / LPT;  // tokens per wavefront
+    const int tid = threadIdx.x;
+    const int n_tiles = (T + 63) >> 6;
+    for (int q = tid; q < SMALL_TILES * 256; q += 1024) (&tmask[0][0])[q] = 0ull;
+    __syncthreads();
+    for (int t_first = (tid >> 6) * TPW; t_first < T; t_first += 16 * TPW)
+        select_group<EJ, LPT>(T, E, K, thr, r, tmask[t_first >> 6], s_mid, t_first, tid & 63);
+    __syncthreads();
+    if (tid < E) {
+        int run = 0;
+        for (int tile = 0; tile < n_tiles; ++tile) {
+            s_base[tile][tid] = run;
+            run += __popcll(tmask[tile][tid]);
+        }
+        s_cnt[tid] = run;
+    }
+    __syncthreads();
+    if (tid < 64) offsets_from_counts(s_cnt, s_off, E, bm, r, meta, tid);
+    __syncthreads();
+    const int TK = T * K;
+    blocks_and_pads(s_off, s_cnt, E, bm, TK, r, tid, 1024);
+    for (int p = tid; p < TK; p += 1024) {
+        const int e = s_mid[p];
+        if (e < 0) {
+            pair_pos[p] = -1;
+            continue;
+        }
+        const int t = p / K;
+        const int tile = t >> 6;
+        const int pos =
+            s_off[e] + s_base[tile][e] + __popcll(tmask[tile][e] & ((1ull << (t & 63)) - 1ull));
+        place_pair(p, e, pos, K, r, pair_pos, sorted_tok);
+    }
 }
 
 hipError_t launch_router_logits(const Plan &p, const void *x, const void *Wg, const void *Wm,
-                                const Work &w, hipStream_t s) {
+                                const Routing &r, hipStream_t s) {
     if (p.dtype == 1) {
-        const dim3 grid((p.T + p.r_tt - 1) / p.r_tt, (2 * p.E + 63) / 64, p.r_splits);
-        if (p.r_tt == 16)
-            router_logits_bf16<1><<<grid, 256, 0, s>>>((const bf16_t *)x, (const bf16_t *)Wg,
-                                                       (const bf16_t *)Wm, w.partial, p.T, p.d,
-                                                       p.E, p.r_dchunk);
-        else
-            router_logits_bf16<4><<<grid, 256, 0, s>>>((const bf16_t *)x, (const bf16_t *)Wg,
-                                                       (const bf16_t *)Wm, w.partial, p.T, p.d,
-                                                       p.E, p.r_dchunk);
+        const int mt = p.T <= 16 ? 1 : 2;
+        const dim3 grid((p.T + 16 * mt - 1) / (16 * mt), (2 * p.E + 15) / 16);
+#define BEAM_ROUTER(MTV, NWV)                                                                  \
+    router_logits_bf16<MTV, NWV><<<grid, NWV * 64, 0, s>>>(                                  \
+        (const bf16_t *)x, (const bf16_t *)Wg, (const bf16_t *)Wm, r.gate_logits,            \
+        r.mask_logits, p.T, p.d, p.E)
+        if (p.d % 256 == 0) {
+            if (mt == 1) BEAM_ROUTER(1, 8); else BEAM_ROUTER(2, 8);
+        } else {
+            if (mt == 1) BEAM_ROUTER(1, 4); else BEAM_ROUTER(2, 4);
+        }
+#undef BEAM_ROUTER
     } else {
         const long long n = (long long)p.T * 2 * p.E;
         router_logits_generic<float><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
-            (const float *)x, (const float *)Wg, (const float *)Wm, w.partial, p.T, p.d, p.E);
+            (const float *)x, (const float *)Wg, (const float *)Wm, r.gate_logits, r.mask_logits,
+            p.T, p.d, p.E);
     }
     return hipGetLastError();
 }
 
+template <int EJ, int LPT>
+static void launch_select_t(const Plan &p, const Routing &r, const Work &w, hipStream_t s) {
+    if (p.small_route)
+        route_small<EJ, LPT><<<1, 1024, 0, s>>>(p.T, p.E, p.K, p.thr, p.bm, r, w.pair_pos, w.meta,
+                                               w.sorted_tok);
+    else
+        select_topk_mask<EJ, LPT><<<p.n_tiles, LPT * 64, 0, s>>>(p.T, p.E, p.K, p.thr, r,
+                                                               w.tile_mask);
+}
+
+template <int LPT>
+static void launch_select_l(const Plan &p, const Routing &r, const Work &w, hipStream_t s) {
+    // experts per lane: E / LPT rounded up to a power of two
+    const int ej = (p.E + LPT - 1) / LPT;
+    if (ej <= 1) launch_select_t<1, LPT>(p, r, w, s);
+    else if (ej <= 2) launch_select_t<2, LPT>(p, r, w, s);
+    else if (ej <= 4) launch_select_t<4, LPT>(p, r, w, s);
+    else if (ej <= 8) launch_select_t<8, LPT>(p, r, w, s);
+    else if (ej <= 16) launch_select_t<16, LPT>(p, r, w, s);
+    else if (ej <= 32) launch_select_t<32, LPT>(p, r, w, s);
+    else launch_select_t<64, LPT>(p, r, w, s);
+}
+
 hipError_t launch_select(const Plan &p, const Routing &r, const Work &w, hipStream_t s) {
-    select_topk_mask<<<p.n_tiles, 256, 0, s>>>(w.partial, p.r_splits, p.T, p.E, p.K, p.thr, r,
-                                               w.tile_mask);
+    // few tokens: 16 lanes per token (shortest latency); more: 4 lanes per
+    // token (a quarter of the instructions per token)
+    if (p.T <= 32) launch_select_l<16>(p, r, w, s);
+    else launch_select_l<4>(p, r, w, s);
     return hipGetLastError();
 }
 

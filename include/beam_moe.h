@@ -50,7 +50,8 @@ extern "C" {
 /* status codes */
 #define BEAM_OK            0
 #define BEAM_EINVAL       (-1) /* null/misaligned pointer, bad sizes, K > E ...   */
-#define BEAM_EUNSUPPORTED (-2) /* valid but outside kernel coverage (see query)   */
+#define BEAM_EUNSUPPORTED (-2) /* valid but outside kernel coverage: E > 256,
+                                  K > 16, or (bf16) d % 128, I % 64, I > 2040     */
 #define BEAM_EWORKSPACE   (-3) /* workspace too small                              */
 #define BEAM_EHIP         (-4) /* a HIP launch failed                              */
 
@@ -139,10 +140,12 @@ int beam_moe_forward(const beam_moe_desc *desc, const void *x, const void *W_gat
                      hipStream_t stream);
 
 /* beam_moe_forward_ex: beam_moe_forward plus optional per-stage events.
- * stage_events: NULL, or BEAM_NUM_STAGES + 1 events created by the caller;
- * event i is recorded on `stream` just before stage i is enqueued and event
- * BEAM_NUM_STAGES after the last stage (a stage that the chosen path fuses
- * into another one, or skips, has equal start and end events). */
+ * stage_events: NULL, or an array of BEAM_NUM_STAGES + 1 entries, each a
+ * caller-created event or NULL (not recorded); event i is recorded on
+ * `stream` just before stage i is enqueued and event BEAM_NUM_STAGES after
+ * the last stage (a stage that the chosen path fuses into another one, or
+ * skips, has equal start and end events).  Each record is a separate stream
+ * command and adds a few microseconds between the stages it separates. */
 int beam_moe_forward_ex(const beam_moe_desc *desc, const void *x, const void *W_gate,
                         const void *W_mask, const void *W_gu, const void *W_dt,
                         void *y, const beam_moe_routing *out, void *ws,
