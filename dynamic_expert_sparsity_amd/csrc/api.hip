@@ -72,8 +72,7 @@ int make_plan(const beam_moe_desc *desc, Plan &p) {
 
     p.s_ts = 64;
     p.n_tiles = (D.T + 63) / 64;
-    p.small_route = D.T <= 256;
-    p.fuse_scatter = !p.small_route && p.n_tiles <= 16;
+    p.fuse_scatter = p.n_tiles <= 16;
     p.max_active = (int)(TK < D.E ? TK : D.E);
     const long long cap_raw = TK + (long long)p.max_active * (p.bm - 1);
     p.cap = (cap_raw + p.bm - 1) / p.bm * p.bm;
@@ -142,13 +141,11 @@ struct Events {
 int enqueue_route(const Plan &p, const void *x, const void *Wg, const void *Wm, const Routing &r,
                   const Work &w, hipStream_t s, const Events &ev) {
     BEAM_TRY(ev.mark(BEAM_STAGE_ROUTER), "event");
-    BEAM_TRY(launch_router_logits(p, x, Wg, Wm, r, s), "router logits");
+    BEAM_TRY(launch_route(p, x, Wg, Wm, r, w, s), "routing");
     BEAM_TRY(ev.mark(BEAM_STAGE_SELECT), "event");
-    BEAM_TRY(launch_select(p, r, w, s), "select");
     BEAM_TRY(ev.mark(BEAM_STAGE_SCAN), "event");
-    if (!p.small_route) BEAM_TRY(launch_scan(p, r, w, s), "compaction scan");
     BEAM_TRY(ev.mark(BEAM_STAGE_SCATTER), "event");
-    if (!p.small_route) BEAM_TRY(launch_scatter(p, r, w, s), "compaction scatter");
+    BEAM_TRY(launch_scatter(p, r, w, s), "compaction scatter");
     return BEAM_OK;
 }
 

@@ -1,7 +1,16 @@
-// Device-side pieces of the grouping of active pairs, shared by the
-// multi-tile compaction kernels and the single-workgroup small-batch routing
-// kernel.  Masked slots (id -1) are left out of every count, so masked pairs
-// are never scheduled (news article on the BEAM paper, section 5).
+// Device-side grouping of the active (token, expert) pairs into per-expert
+// lists.  Masked slots (id -1) are left out of every count, so masked pairs
+// are never scheduled (news article on the BEAM paper, section 5, the
+// modified expert/token grouping kernel).
+//
+// Input: per select tile (64 tokens) and expert, the 64-bit set of tile
+// tokens that have an active pair for that expert (an expert appears at most
+// once among a token's K slots).
+//   count(tile, e)        = popcount(set)
+//   rank of token tl      = popcount(set & ((1 << tl) - 1))
+// so a pair's position in its expert's list is
+//   offsets[e] + (pairs of e in earlier tiles) + rank,
+// which lists each expert's pairs in ascending pair id with no atomics.
 #pragma once
 #include "common.h"
 #include "kernels.h"
@@ -95,6 +104,67 @@ __device__ __forceinline__ void place_pair(int p, int e, int pos, int K, const R
     r.sorted_pairs[pos] = p;
     sorted_tok[pos] = p / K;
     pair_pos[p] = pos;
+}
+
+__device__ __forceinline__ void scatter_pair(int p, int K, int E, const Routing &r,
+                                             const int *off, const int32_t *tile_base,
+                                             const uint64_t *tile_mask, int32_t *pair_pos,
+                                             int32_t *sorted_tok) {
+    const int e = r.masked_ids[p];
+    if (e < 0) {
+        pair_pos[p] = -1;
+        return;
+    }
+    const int t = p / K;
+    const size_t q = (size_t)(t >> 6) * E + e;
+    const int rank = __popcll(tile_mask[q] & ((1ull << (t & 63)) - 1ull));
+    place_pair(p, e, off[e] + tile_base[q] + rank, K, r, pair_pos, sorted_tok);
+}
+
+// Whole-batch compaction by one workgroup of `nthreads` (>= E) threads.
+// Thread (g, e), g = tid / E, sums the popcounts of a contiguous range of
+// tiles for expert e; group partials give every (tile, expert) its base;
+// wave 0 scans the experts into block-padded offsets; then the block map and
+// pads, and (do_scatter) the position of every pair.  LDS: s_part[nthreads],
+// s_cnt[256], s_off[257].
+__device__ __forceinline__ void scan_tiles(const uint64_t *tile_mask, int n_tiles, int E, int bm,
+                                           int K, int TK, const Routing &r, int32_t *tile_base,
+                                           int32_t *pair_pos, int32_t *meta, int32_t *sorted_tok,
+                                           bool do_scatter, int tid, int nthreads, int *s_part,
+                                           int *s_cnt, int *s_off) {
+    const int NG = nthreads / E;
+    const int g = tid / E;
+    const int e = tid - g * E;
+    const bool on = g < NG;
+    const int chunk = (n_tiles + NG - 1) / NG;
+    const int tb = g * chunk;
+    const int te = min(n_tiles, tb + chunk);
+
+    int local = 0;
+    if (on)
+        for (int t = tb; t < te; ++t) local += __popcll(tile_mask[(size_t)t * E + e]);
+    s_part[tid] = local;
+    __syncthreads();
+    if (on) {
+        int base = 0, total = 0;
+        for (int q = 0; q < NG; ++q) {
+            const int v = s_part[q * E + e];
+            if (q < g) base += v;
+            total += v;
+        }
+        for (int t = tb; t < te; ++t) {
+            tile_base[(size_t)t * E + e] = base;
+            base += __popcll(tile_mask[(size_t)t * E + e]);
+        }
+        if (g == 0) s_cnt[e] = total;
+    }
+    __syncthreads();
+    if (tid < 64) offsets_from_counts(s_cnt, s_off, E, bm, r, meta, tid);
+    __syncthreads();
+    blocks_and_pads(s_off, s_cnt, E, bm, TK, r, tid, nthreads);
+    if (do_scatter)
+        for (int p = tid; p < TK; p += nthreads)
+            scatter_pair(p, K, E, r, s_off, tile_base, tile_mask, pair_pos, sorted_tok);
 }
 
 }  // namespace beam

@@ -16,8 +16,7 @@ struct Plan {
     // select / compaction
     int s_ts;           // tokens per select tile (64)
     int n_tiles;        // ceil(T / s_ts)
-    int small_route;    // T <= 256: select + compaction in one workgroup
-    int fuse_scatter;   // few tiles: the scan workgroup also places the pairs
+    int fuse_scatter;   // T <= 1024: the compaction workgroup also places the pairs
     long long cap;          // sorted_pairs capacity
     long long n_blocks_cap; // block_expert capacity
     int max_active;     // host upper bound on experts with >= 1 active pair
@@ -47,10 +46,10 @@ struct Work {  // workspace views
     void *o;
 };
 
-hipError_t launch_router_logits(const Plan &p, const void *x, const void *Wg, const void *Wm,
-                                const Routing &r, hipStream_t s);
-hipError_t launch_select(const Plan &p, const Routing &r, const Work &w, hipStream_t s);
-hipError_t launch_scan(const Plan &p, const Routing &r, const Work &w, hipStream_t s);
+// router logits, select and compaction
+hipError_t launch_route(const Plan &p, const void *x, const void *Wg, const void *Wm,
+                        const Routing &r, const Work &w, hipStream_t s);
+// pair scatter for large batches (no-op when the routing kernel placed them)
 hipError_t launch_scatter(const Plan &p, const Routing &r, const Work &w, hipStream_t s);
 hipError_t launch_expert_up(const Plan &p, const void *x, const void *W_gu, const Routing &r,
                             const Work &w, hipStream_t s);

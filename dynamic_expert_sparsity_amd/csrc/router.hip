@@ -1,40 +1,48 @@
-// a1-a3: router logits (main router and mask router in one pass), then per
-// token Top-K, softmax over the kept logits, binary mask, g_hat and -1 ids.
+// a1-a4: router logits (main router and mask router in one pass), then per
+// token Top-K, softmax over the kept logits, binary mask, g_hat and -1 ids,
+// then the grouping of the active pairs.
 //
 // BEAM paper, section 3.2: Eq. 4 (r = R(x), Top-K, Softmax over the kept K),
 // Eq. 5 (z = x W_m), Eq. 6 (m = [sigmoid(z) >= 0.5], evaluated as z >= 0),
 // Eq. 7 (g_hat = g * m, no renormalisation).  Masked slots get the expert id
-// -1 (news article on the paper, section 5, the modified routing kernel).
+// -1 and are left out of the per-expert counts (news article on the paper,
+// section 5, the two modified kernels).
+//
+// Kernels: the logits (many workgroups, each a 16-column block), then either
+// one workgroup that selects and groups a small batch, or one workgroup per
+// 64-token tile for the select and one workgroup for the grouping.
 #include "compact_dev.h"
 
 namespace beam {
 
 // ---------------------------------------------------------------------------
-// Router logits, bf16, MFMA 16x16x32.  The two routers are one GEMM with
-// 2E output columns: column n < E is W_gate row n, column E + n is W_mask
-// row n.  A workgroup owns 16 columns and 16*MT tokens; its NW waves split d
-// (every wave requests all of its x and weight fragments before the first
-// MFMA) and their partial sums meet in LDS, where wave 0 adds them in wave
-// order and writes the finished float32 logits.  A (x rows) and B (weight
-// rows) are both k-contiguous, so every lane's 16-byte load lands directly
-// in MFMA layout.  Out-of-range tokens / columns load a clamped row and their
-// results are not stored.
+// Router logits block, bf16, MFMA 16x16x32.  The two routers are one GEMM
+// with 2E output columns: column n < E is W_gate row n, column E + n is
+// W_mask row n.  A workgroup owns 16 columns and 16*MT tokens; its NW waves
+// split d (every wave requests all of its x and weight fragments before the
+// first MFMA) and their partial sums meet in LDS, where wave 0 adds them in
+// wave order and writes the finished float32 logits.  A (x rows) and B
+// (weight rows) are both k-contiguous, so every lane's 16-byte load lands
+// directly in MFMA layout.  Out-of-range tokens / columns load a clamped row
+// and their results are not stored.
 // ---------------------------------------------------------------------------
 template <int MT, int NW>
 __global__ __launch_bounds__(NW * 64) void router_logits_bf16(
-    const bf16_t *__restrict__ x, const bf16_t *__restrict__ Wg,
-    const bf16_t *__restrict__ Wm, float *__restrict__ gate_logits,
-    float *__restrict__ mask_logits, int T, int d, int E) {
+    const bf16_t *__restrict__ x, const bf16_t *__restrict__ Wg, const bf16_t *__restrict__ Wm,
+    float *__restrict__ gate_logits, float *__restrict__ mask_logits, int T, int d, int E) {
+    __shared__ f32x4 red[NW][MT][64];
+    const int rtile = blockIdx.x;
+    const int cgroup = blockIdx.y;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int twoE = 2 * E;
-    const int n = blockIdx.y * 16 + (lane & 15);
+    const int n = cgroup * 16 + (lane & 15);
     const int nc = n < twoE ? n : twoE - 1;
     const int kq = (lane >> 4) * 8;
     const int dq = d / NW;
     const int kb = wave * dq + kq;
     const bf16_t *brow = (nc < E ? Wg + (size_t)nc * d : Wm + (size_t)(nc - E) * d) + kb;
-    const int tbase = blockIdx.x * 16 * MT;
+    const int tbase = rtile * 16 * MT;
 
     const bf16_t *arow[MT];
 #pragma unroll
@@ -68,7 +76,6 @@ __global__ __launch_bounds__(NW * 64) void router_logits_bf16(
                 for (int m = 0; m < MT; ++m) acc[m] = mfma16x16x32(a[c][m], b[c], acc[m]);
     }
 
-    __shared__ f32x4 red[NW][MT][64];
 #pragma unroll
     for (int m = 0; m < MT; ++m) red[wave][m][lane] = acc[m];
     __syncthreads();
@@ -87,8 +94,8 @@ __global__ __launch_bounds__(NW * 64) void router_logits_bf16(
     }
 }
 
-// Router logits, any element type, plain float dot products (used for the
-// float32 layer).  One thread per (token, column).
+// Router logits, float32 layer: plain float dot products, one thread per
+// (token, column).
 template <typename T_>
 __global__ __launch_bounds__(256) void router_logits_generic(
     const T_ *__restrict__ x, const T_ *__restrict__ Wg, const T_ *__restrict__ Wm,
@@ -265,7 +272,7 @@ __device__ __forceinline__ void select_group(int T, int E, int K, float thr, con
     }
 }
 
-// One workgroup per 64-token tile: LPT waves of 64/LPT tokens each.
+// One workgroup per 64-token tile: the select, and the tile's token sets.
 template <int EJ, int LPT>
 __global__ __launch_bounds__(LPT * 64) void select_topk_mask(int T, int E, int K, float thr,
                                                              Routing r,
@@ -280,37 +287,41 @@ __global__ __launch_bounds__(LPT * 64) void select_topk_mask(int T, int E, int K
     for (int e = tid; e < E; e += LPT * 64) tile_mask[(size_t)blockIdx.x * E + e] = tmask[e];
 }
 
-// T <= 256 (at most 4 tiles): select, counts, offsets, lists and pair
-// positions in one workgroup of 1024 threads; the tile sets and the masked
-// ids stay in LDS.
-constexpr int SMALL_TILES = 4;
+// The grouping of a batch of tiles by one workgroup (and the pair positions
+// when the batch is small).
+__global__ __launch_bounds__(1024) void compact_tiles(const uint64_t *__restrict__ tile_mask,
+                                                      int n_tiles, int E, int bm, int K, int TK,
+                                                      Routing r, int32_t *__restrict__ tile_base,
+                                                      int32_t *__restrict__ pair_pos,
+                                                      int32_t *__restrict__ meta,
+                                                      int32_t *__restrict__ sorted_tok,
+                                                      int fuse_scatter) {
+    __shared__ int s_part[1024];
+    __shared__ int s_cnt[256];
+    __shared__ int s_off[257];
+    scan_tiles(tile_mask, n_tiles, E, bm, K, TK, r, tile_base, pair_pos, meta, sorted_tok,
+               fuse_scatter != 0, threadIdx.x, 1024, s_part, s_cnt, s_off);
+}
 
+// A small batch (T <= 64, one tile) in one workgroup: select, counts,
+// offsets, lists and pair positions; the token sets and masked ids stay in LDS.
 template <int EJ, int LPT>
 __global__ __launch_bounds__(1024) void route_small(int T, int E, int K, float thr, int bm,
                                                     Routing r, int32_t *__restrict__ pair_pos,
                                                     int32_t *__restrict__ meta,
                                                     int32_t *__restrict__ sorted_tok) {
-    __shared__ unsigned long long tmask[SMALL_TILES][256];
-    __shared__ int s_mid[SMALL_TILES * 64 * 16];
-    __shared__ int s_base[SMALL_TILES][256];
+    __shared__ unsigned long long tmask[256];
+    __shared__ int s_mid[64 * 16];
     __shared__ int s_cnt[256];
     __shared__ int s_off[257];
     constexpr int TPW = 64 / LPT;  // tokens per wavefront
     const int tid = threadIdx.x;
-    const int n_tiles = (T + 63) >> 6;
-    for (int q = tid; q < SMALL_TILES * 256; q += 1024) (&tmask[0][0])[q] = 0ull;
+    if (tid < E) tmask[tid] = 0ull;
     __syncthreads();
     for (int t_first = (tid >> 6) * TPW; t_first < T; t_first += 16 * TPW)
-        select_group<EJ, LPT>(T, E, K, thr, r, tmask[t_first >> 6], s_mid, t_first, tid & 63);
+        select_group<EJ, LPT>(T, E, K, thr, r, tmask, s_mid, t_first, tid & 63);
     __syncthreads();
-    if (tid < E) {
-        int run = 0;
-        for (int tile = 0; tile < n_tiles; ++tile) {
-            s_base[tile][tid] = run;
-            run += __popcll(tmask[tile][tid]);
-        }
-        s_cnt[tid] = run;
-    }
+    if (tid < E) s_cnt[tid] = __popcll(tmask[tid]);
     __syncthreads();
     if (tid < 64) offsets_from_counts(s_cnt, s_off, E, bm, r, meta, tid);
     __syncthreads();
@@ -323,16 +334,44 @@ __global__ __launch_bounds__(1024) void route_small(int T, int E, int K, float t
             continue;
         }
         const int t = p / K;
-        const int tile = t >> 6;
-        const int pos =
-            s_off[e] + s_base[tile][e] + __popcll(tmask[tile][e] & ((1ull << (t & 63)) - 1ull));
-        place_pair(p, e, pos, K, r, pair_pos, sorted_tok);
+        place_pair(p, e, s_off[e] + __popcll(tmask[e] & ((1ull << t) - 1ull)), K, r, pair_pos,
+                   sorted_tok);
     }
 }
 
-hipError_t launch_router_logits(const Plan &p, const void *x, const void *Wg, const void *Wm,
-                                const Routing &r, hipStream_t s) {
+template <int EJ, int LPT>
+static void launch_select_t(const Plan &p, const Routing &r, const Work &w, hipStream_t s) {
+    if (p.T <= 64) {
+        route_small<EJ, LPT><<<1, 1024, 0, s>>>(p.T, p.E, p.K, p.thr, p.bm, r, w.pair_pos, w.meta,
+                                               w.sorted_tok);
+    } else {
+        select_topk_mask<EJ, LPT><<<p.n_tiles, LPT * 64, 0, s>>>(p.T, p.E, p.K, p.thr, r,
+                                                               w.tile_mask);
+        compact_tiles<<<1, 1024, 0, s>>>(w.tile_mask, p.n_tiles, p.E, p.bm, p.K, p.T * p.K, r,
+                                         w.tile_base, w.pair_pos, w.meta, w.sorted_tok,
+                                         p.fuse_scatter);
+    }
+}
+
+template <int LPT>
+static void launch_select_l(const Plan &p, const Routing &r, const Work &w, hipStream_t s) {
+    // experts per select lane: E / LPT rounded up to a power of two
+    const int ej = (p.E + LPT - 1) / LPT;
+    if (ej <= 1) launch_select_t<1, LPT>(p, r, w, s);
+    else if (ej <= 2) launch_select_t<2, LPT>(p, r, w, s);
+    else if (ej <= 4) launch_select_t<4, LPT>(p, r, w, s);
+    else if (ej <= 8) launch_select_t<8, LPT>(p, r, w, s);
+    else if (ej <= 16) launch_select_t<16, LPT>(p, r, w, s);
+    else if constexpr (LPT == 4) {
+        if (ej <= 32) launch_select_t<32, LPT>(p, r, w, s);
+        else launch_select_t<64, LPT>(p, r, w, s);
+    }
+}
+
+hipError_t launch_route(const Plan &p, const void *x, const void *Wg, const void *Wm,
+                        const Routing &r, const Work &w, hipStream_t s) {
     if (p.dtype == 1) {
+        // few tokens: 16-token router tiles; more: 32-token tiles
         const int mt = p.T <= 16 ? 1 : 2;
         const dim3 grid((p.T + 16 * mt - 1) / (16 * mt), (2 * p.E + 15) / 16);
 #define BEAM_ROUTER(MTV, NWV)                                                                  \
@@ -351,35 +390,10 @@ hipError_t launch_router_logits(const Plan &p, const void *x, const void *Wg, co
             (const float *)x, (const float *)Wg, (const float *)Wm, r.gate_logits, r.mask_logits,
             p.T, p.d, p.E);
     }
-    return hipGetLastError();
-}
-
-template <int EJ, int LPT>
-static void launch_select_t(const Plan &p, const Routing &r, const Work &w, hipStream_t s) {
-    if (p.small_route)
-        route_small<EJ, LPT><<<1, 1024, 0, s>>>(p.T, p.E, p.K, p.thr, p.bm, r, w.pair_pos, w.meta,
-                                               w.sorted_tok);
-    else
-        select_topk_mask<EJ, LPT><<<p.n_tiles, LPT * 64, 0, s>>>(p.T, p.E, p.K, p.thr, r,
-                                                               w.tile_mask);
-}
-
-template <int LPT>
-static void launch_select_l(const Plan &p, const Routing &r, const Work &w, hipStream_t s) {
-    // experts per lane: E / LPT rounded up to a power of two
-    const int ej = (p.E + LPT - 1) / LPT;
-    if (ej <= 1) launch_select_t<1, LPT>(p, r, w, s);
-    else if (ej <= 2) launch_select_t<2, LPT>(p, r, w, s);
-    else if (ej <= 4) launch_select_t<4, LPT>(p, r, w, s);
-    else if (ej <= 8) launch_select_t<8, LPT>(p, r, w, s);
-    else if (ej <= 16) launch_select_t<16, LPT>(p, r, w, s);
-    else if (ej <= 32) launch_select_t<32, LPT>(p, r, w, s);
-    else launch_select_t<64, LPT>(p, r, w, s);
-}
-
-hipError_t launch_select(const Plan &p, const Routing &r, const Work &w, hipStream_t s) {
-    // few tokens: 16 lanes per token (shortest latency); more: 4 lanes per
-    // token (a quarter of the instructions per token)
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    // few tokens: 16 select lanes per token (shortest latency); more: 4 lanes
+    // per token (a quarter of the instructions per token)
     if (p.T <= 32) launch_select_l<16>(p, r, w, s);
     else launch_select_l<4>(p, r, w, s);
     return hipGetLastError();

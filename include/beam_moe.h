@@ -64,10 +64,11 @@ extern "C" {
 #define BEAM_FORCE_PREFILL  (1u << 1) /* LDS-tiled grouped-GEMM expert kernels     */
 
 /* stage ids for the optional per-stage events of beam_moe_forward_ex */
-#define BEAM_STAGE_ROUTER   0 /* a1: router logits (both routers)                 */
-#define BEAM_STAGE_SELECT   1 /* a2-a3: top-K, softmax, mask, g_hat, -1 ids       */
-#define BEAM_STAGE_SCAN     2 /* a4: per-expert counts, offsets, lists metadata   */
-#define BEAM_STAGE_SCATTER  3 /* a4: pairs into per-expert sorted lists           */
+#define BEAM_STAGE_ROUTER   0 /* a1-a4: router logits, top-K, softmax, mask,
+                                 g_hat, -1 ids, counts, offsets, lists            */
+#define BEAM_STAGE_SELECT   1 /* (inside BEAM_STAGE_ROUTER: empty)                */
+#define BEAM_STAGE_SCAN     2 /* (inside BEAM_STAGE_ROUTER: empty)                */
+#define BEAM_STAGE_SCATTER  3 /* a4: pairs into per-expert lists, T > 1024 only   */
 #define BEAM_STAGE_UP       4 /* a5: expert gate/up projections + SiLU * up       */
 #define BEAM_STAGE_DOWN     5 /* a6: expert down projection                       */
 #define BEAM_STAGE_COMBINE  6 /* a7: masked weighted sum                          */
