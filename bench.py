@@ -55,6 +55,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle sample")
+    ap.add_argument("--only-headline", action="store_true",
+                    help="measure the headline workload only (no all-ones run, no sweep)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (torch) three times, so that "
+                         "hardware byte counters can be scaled by a copy of known size")
     return ap.parse_args()
 
 
@@ -203,10 +208,23 @@ def main():
         del Ls
         return r
 
+    if args.calibrate_copy:
+        src = torch.ones(1 << 29, dtype=torch.int16, device=dev)   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 copies of 1 GiB (1073741824 bytes read and written each)")
+        del src, dst
+
     # ---- headline --------------------------------------------------------
     log(f"headline: T={args.T}, {args.steps} steps after {args.warmup} warm-up")
     head = measure(args.T, args.steps, args.warmup, kernels=("up", "down"))
-    ones = measure(args.T, args.steps, args.warmup, allones=True, kernels=("up", "down"))
+    ones = None
+    if not args.only_headline:
+        ones = measure(args.T, args.steps, args.warmup, allones=True, kernels=("up", "down"))
+    else:
+        sweep = []
     km = head["kernel_ms"]
     dom = max(km, key=km.get)
     alg = head["_alg"]
@@ -261,12 +279,13 @@ def main():
         "layer_hbm": {"bytes": head["layer_bytes"], "GBps": round(head["layer_GBps"], 1),
                       "frac": round(head["layer_hbm_frac"], 4)},
         "stages_ms_evented": _r(head["stages_ms_evented"]),
-        "allones": {"ms_per_step": round(ones["ms_per_step"], 5),
-                    "tok_per_s": round(ones["tok_per_s"], 1),
-                    "active_experts": ones["active_experts"],
-                    "layer_bytes": ones["layer_bytes"],
-                    "kernel_ms": _r(ones["kernel_ms"]),
-                    "speedup_masked_vs_allones": round(ones["ms_per_step"] / head["ms_per_step"], 3)},
+        "allones": None if ones is None else {
+            "ms_per_step": round(ones["ms_per_step"], 5),
+            "tok_per_s": round(ones["tok_per_s"], 1),
+            "active_experts": ones["active_experts"],
+            "layer_bytes": ones["layer_bytes"],
+            "kernel_ms": _r(ones["kernel_ms"]),
+            "speedup_masked_vs_allones": round(ones["ms_per_step"] / head["ms_per_step"], 3)},
         "sweep": sweep_out,
         "cpu_baseline": cpu,
     }
