@@ -57,15 +57,23 @@ int make_plan(const beam_moe_desc *desc, Plan &p) {
     if (D.dtype == BEAM_BF16 && (D.d % 128 != 0 || D.I % 64 != 0 || D.I > 2040))
         return fail(BEAM_EUNSUPPORTED,
                     "bf16 layer needs d %% 128 == 0, I %% 64 == 0 and I <= 2040 (d=%d I=%d)", D.d, D.I);
-    if (D.flags & BEAM_FORCE_PREFILL)
-        return fail(BEAM_EUNSUPPORTED, "the tiled prefill path is not available in this build");
+    // the tiled (prefill) path: bf16, 128-position blocks, d % 256, I % 128
+    const bool gemm_ok = D.dtype == BEAM_BF16 && D.d % 256 == 0 && D.I % 128 == 0 &&
+                         (D.block_m == 0 || D.block_m == 128);
+    if ((D.flags & BEAM_FORCE_PREFILL) && !gemm_ok)
+        return fail(BEAM_EUNSUPPORTED,
+                    "the tiled path needs bf16, d %% 256 == 0, I %% 128 == 0, block_m 0 or 128");
     const long long TK = (long long)D.T * D.K;
     if (TK > (1ll << 30)) return fail(BEAM_EUNSUPPORTED, "T*K=%lld too large", TK);
 
     p.T = D.T; p.d = D.d; p.E = D.E; p.K = D.K; p.I = D.I;
     p.dtype = D.dtype;
-    p.path = 0;
-    p.bm = D.block_m ? D.block_m : 16;
+    // decode (weight streaming) for small batches, tiled grouped GEMM above
+    p.path = (D.flags & BEAM_FORCE_PREFILL) ||
+                     (!(D.flags & BEAM_FORCE_DECODE) && gemm_ok && D.T > 512)
+                 ? 1
+                 : 0;
+    p.bm = p.path == 1 ? 128 : (D.block_m ? D.block_m : 16);
     const float tau = D.tau == 0.f ? 0.5f : D.tau;
     // m = [sigmoid(z) >= tau]  <=>  z >= ln(tau / (1 - tau)); exactly 0 at tau = 0.5
     p.thr = tau == 0.5f ? 0.f : (float)std::log((double)tau / (1.0 - (double)tau));

@@ -80,10 +80,11 @@ __device__ __forceinline__ void offsets_from_counts(const int *s_cnt, int *s_off
     }
 }
 
-// All threads: block -> expert map and the pad entries (value TK) of every
-// expert's segment, one thread per block of bm slots.
+// All threads: block -> expert map and the pad entries of every expert's
+// segment (sorted pair TK, token 0), one thread per block of bm slots.
 __device__ __forceinline__ void blocks_and_pads(const int *s_off, const int *s_cnt, int E, int bm,
-                                                int TK, const Routing &r, int tid, int nthreads) {
+                                                int TK, const Routing &r, int32_t *sorted_tok,
+                                                int tid, int nthreads) {
     const int n_blocks = s_off[E] / bm;
     for (int b = tid; b < n_blocks; b += nthreads) {
         const int pos = b * bm;
@@ -94,7 +95,10 @@ __device__ __forceinline__ void blocks_and_pads(const int *s_off, const int *s_c
         }
         r.block_expert[b] = lo;
         const int end_valid = s_off[lo] + s_cnt[lo];
-        for (int q = max(pos, end_valid); q < pos + bm; ++q) r.sorted_pairs[q] = TK;
+        for (int q = max(pos, end_valid); q < pos + bm; ++q) {
+            r.sorted_pairs[q] = TK;
+            sorted_tok[q] = 0;
+        }
     }
 }
 
@@ -161,7 +165,7 @@ __device__ __forceinline__ void scan_tiles(const uint64_t *tile_mask, int n_tile
     __syncthreads();
     if (tid < 64) offsets_from_counts(s_cnt, s_off, E, bm, r, meta, tid);
     __syncthreads();
-    blocks_and_pads(s_off, s_cnt, E, bm, TK, r, tid, nthreads);
+    blocks_and_pads(s_off, s_cnt, E, bm, TK, r, sorted_tok, tid, nthreads);
     if (do_scatter)
         for (int p = tid; p < TK; p += nthreads)
             scatter_pair(p, K, E, r, s_off, tile_base, tile_mask, pair_pos, sorted_tok);

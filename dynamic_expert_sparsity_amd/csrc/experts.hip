@@ -306,6 +306,7 @@ __global__ __launch_bounds__(256) void combine_bf16(const bf16_t *__restrict__ o
 
 hipError_t launch_expert_up(const Plan &p, const void *x, const void *W_gu, const Routing &r,
                             const Work &w, hipStream_t s) {
+    if (p.path == 1) return launch_gemm_up(p, x, W_gu, r, w, s);
     if (p.dtype == 1) {
         const unsigned grid = (unsigned)p.max_active * (unsigned)(p.I / 16);
 #define BEAM_UP(NWV, NKV)                                                                     \
@@ -337,6 +338,7 @@ hipError_t launch_expert_up(const Plan &p, const void *x, const void *W_gu, cons
 
 hipError_t launch_expert_down(const Plan &p, const void *W_dt, const Routing &r, const Work &w,
                               hipStream_t s) {
+    if (p.path == 1) return launch_gemm_down(p, W_dt, r, w, s);
     if (p.dtype == 1) {
         const unsigned grid = (unsigned)p.max_active * (unsigned)(p.d / 64);
         const size_t lds = (size_t)16 * (p.I + 8) * sizeof(bf16_t);

@@ -326,7 +326,7 @@ __global__ __launch_bounds__(1024) void route_small(int T, int E, int K, float t
     if (tid < 64) offsets_from_counts(s_cnt, s_off, E, bm, r, meta, tid);
     __syncthreads();
     const int TK = T * K;
-    blocks_and_pads(s_off, s_cnt, E, bm, TK, r, tid, 1024);
+    blocks_and_pads(s_off, s_cnt, E, bm, TK, r, sorted_tok, tid, 1024);
     for (int p = tid; p < TK; p += 1024) {
         const int e = s_mid[p];
         if (e < 0) {

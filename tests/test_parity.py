@@ -93,3 +93,38 @@ def test_zero_tokens():
     y, R = lay(L["x"])
     torch.cuda.synchronize()
     assert y.shape == (0, 128)
+
+
+# ---- the tiled (prefill) path: grouped MFMA GEMMs over 128-position blocks --
+GEMM_SMALL = synth.LayerShape(256, 8, 2, 128, torch.bfloat16)
+
+
+@pytest.mark.parametrize("T", [1, 50, 300, 700])
+def test_prefill_path_small(T):
+    import dynamic_expert_sparsity_amd as B
+    L = layer(GEMM_SMALL, T, seed=1000 + T, mask_bias=-0.2)
+    y, G, O, _ = _full_check(L, 2, flags=B.BEAM_FORCE_PREFILL)
+
+
+def test_prefill_and_decode_paths_agree():
+    import dynamic_expert_sparsity_amd as B
+    need_gpu()
+    L = layer("qwen3", 600, seed=1100, mask_bias=0.0)
+    yd, Rd, _ = run(L, 8, flags=B.BEAM_FORCE_DECODE)
+    yp, Rp, lay = run(L, 8, flags=B.BEAM_FORCE_PREFILL)
+    assert lay.sizes["path"] == 1 and lay.sizes["block_m"] == 128
+    np.testing.assert_array_equal(Rd["masked_ids"].numpy(), Rp["masked_ids"].numpy())
+    err = np.linalg.norm(yd - yp) / np.linalg.norm(yp)
+    assert err < 5e-3
+
+
+@pytest.mark.parametrize("b", [0.0, 8.0])
+def test_qwen3_prefill_8192(b):
+    L = layer("qwen3", 8192, seed=1200, mask_bias=b)
+    _full_check(L, 8, tokens=sample_tokens(8192, 32, seed=2))
+
+
+@pytest.mark.parametrize("T,b", [(1, -1.04), (64, 0.0), (4096, -1.04)])
+def test_large_layer(T, b):
+    L = layer("large", T, seed=1300 + T, mask_bias=b)
+    _full_check(L, 8, tokens=sample_tokens(T, 24, seed=4))
