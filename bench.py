@@ -55,6 +55,16 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle sample")
+    ap.add_argument("--prefill", default="2048,8192",
+                    help="prefill batch sizes measured at mask biases -1.04/-0.52/0/+8 ('' to skip)")
+    ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--prefill-biases", default="-1.04,-0.52,0,8",
+                    help="mask biases of the prefill runs (keep rate Phi(b))")
+    ap.add_argument("--only-prefill", action="store_true",
+                    help="measure the prefill runs only (no decode headline, sweep or CPU baseline)")
+    ap.add_argument("--skew", action="store_true", default=True,
+                    help="also measure the skewed-load workload (T=16384)")
+    ap.add_argument("--no-skew", dest="skew", action="store_false")
     ap.add_argument("--only-headline", action="store_true",
                     help="measure the headline workload only (no all-ones run, no sweep)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -217,6 +227,64 @@ def main():
         log("copy calibration: 3 copies of 1 GiB (1073741824 bytes read and written each)")
         del src, dst
 
+    # ---- prefill: tiled grouped-GEMM path, MFMA utilisation ---------------
+    def measure_prefill(T, b, skew=False, steps=args.prefill_steps):
+        n = min(2, n_sets)
+        Ls = []
+        for s in range(n):
+            S = sets[s]
+            if skew:
+                Sk = synth.make_layer(shape, T, seed=1, layer=100 + s, skew=True, device=dev)
+                Ls.append((B.MoELayer(Sk["W_gate"], Sk["W_mask"], Sk["W_gu"], Sk["W_dt"], K),
+                           Sk["x"]))
+            else:
+                x = synth.make_tokens(shape, T, seed=0, layer=s, device=dev)
+                Ls.append((B.MoELayer(S["W_gate"], synth.with_mask_bias(S["W_mask"], b),
+                                      S["W_gu"], S["W_dt"], K), x))
+        ms, _ = timed(Ls, steps, 3)
+        kern = {k: timed(Ls, steps, 2, events=k)[1][k] for k in ("router", "up", "down")}
+        cs = counts(Ls)
+        P = sum(c[0] for c in cs) / len(cs)
+        n_act = sum(c[1] for c in cs) / len(cs)
+        alg = algorithmic(n_act, P, T, d, E, I)
+        fl_up = 4.0 * d * I * P
+        fl_dn = 2.0 * d * I * P
+        out = {"T": T, "mask_bias": None if skew else b, "skew": skew,
+               "keep_rate": round(P / (T * K), 4), "active_pairs": P,
+               "ms_per_step": round(ms, 5), "tok_per_s": round(T / (ms * 1e-3), 1),
+               "mfma_frac_layer": round(alg["flops"] / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+               "hbm_frac_layer": round(alg["layer"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+               "kernel_ms": {k: round(v, 5) for k, v in kern.items()},
+               "mfma_frac_up": round(fl_up / (kern["up"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+               "mfma_frac_down": round(fl_dn / (kern["down"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+               # the larger of the two floors: weight bytes at peak HBM, FLOPs at peak MFMA
+               "roofline_ms": round(max(alg["layer"] / (HBM_PEAK_GBPS * 1e9),
+                                        alg["flops"] / (BF16_PEAK_TFLOPS * 1e12)) * 1e3, 5)}
+        out["roofline_frac"] = round(out["roofline_ms"] / ms, 4)
+        del Ls
+        return out
+
+    def run_prefill():
+        prefill_out = []
+        for T in [int(v) for v in args.prefill.split(",") if v.strip()]:
+            for b in [float(v) for v in args.prefill_biases.split(",") if v.strip()]:
+                r = measure_prefill(T, b)
+                prefill_out.append(r)
+                log(f"prefill T={T} b={b:+g}: {r['ms_per_step']*1e3:.1f} us, keep {r['keep_rate']}, "
+                    f"MFMA {r['mfma_frac_layer']:.3f}, roofline {r['roofline_frac']:.3f}")
+        if args.skew:
+            r = measure_prefill(16384, None, skew=True, steps=max(5, args.prefill_steps // 2))
+            prefill_out.append(r)
+            log(f"skew T=16384: {r['ms_per_step']*1e3:.1f} us, keep {r['keep_rate']}, "
+                f"MFMA {r['mfma_frac_layer']:.3f}, roofline {r['roofline_frac']:.3f}")
+        return prefill_out
+
+    if args.only_prefill:
+        prefill_out = run_prefill()
+        print(json.dumps({"metric": METRIC, "unit": "tok/s", "n_gpus": 1, "dtype": "bf16",
+                          "data": "synthetic", "prefill": prefill_out}), flush=True)
+        return
+
     # ---- headline --------------------------------------------------------
     log(f"headline: T={args.T}, {args.steps} steps after {args.warmup} warm-up")
     head = measure(args.T, args.steps, args.warmup, kernels=("up", "down"))
@@ -251,6 +319,8 @@ def main():
         })
         log(f"sweep T={T}: masked {m['ms_per_step']*1e3:.1f} us, "
             f"all-ones {o['ms_per_step']*1e3:.1f} us")
+
+    prefill_out = [] if args.only_headline else run_prefill()
 
     # ---- CPU baseline: the fp64 oracle on this host's cores ---------------
     cpu = None
@@ -287,6 +357,7 @@ def main():
             "kernel_ms": _r(ones["kernel_ms"]),
             "speedup_masked_vs_allones": round(ones["ms_per_step"] / head["ms_per_step"], 3)},
         "sweep": sweep_out,
+        "prefill": prefill_out,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -41,8 +41,9 @@ int make_plan(const beam_moe_desc *desc, Plan &p) {
     if (D.K > D.E) return fail(BEAM_EINVAL, "K=%d exceeds E=%d", D.K, D.E);
     if (D.dtype != BEAM_F32 && D.dtype != BEAM_BF16)
         return fail(BEAM_EINVAL, "dtype %d is neither BEAM_F32 nor BEAM_BF16", D.dtype);
-    if (D.block_m != 0 && D.block_m != 16 && D.block_m != 32 && D.block_m != 64 && D.block_m != 128)
-        return fail(BEAM_EINVAL, "block_m %d is not 0, 16, 32, 64 or 128", D.block_m);
+    if (D.block_m != 0 && D.block_m != 16 && D.block_m != 32 && D.block_m != 64 &&
+        D.block_m != 128 && D.block_m != 256)
+        return fail(BEAM_EINVAL, "block_m %d is not 0, 16, 32, 64, 128 or 256", D.block_m);
     if (D.flags & ~(BEAM_FORCE_DECODE | BEAM_FORCE_PREFILL))
         return fail(BEAM_EINVAL, "unknown flag bits 0x%x", D.flags);
     if ((D.flags & BEAM_FORCE_DECODE) && (D.flags & BEAM_FORCE_PREFILL))
@@ -57,12 +58,12 @@ int make_plan(const beam_moe_desc *desc, Plan &p) {
     if (D.dtype == BEAM_BF16 && (D.d % 128 != 0 || D.I % 64 != 0 || D.I > 2040))
         return fail(BEAM_EUNSUPPORTED,
                     "bf16 layer needs d %% 128 == 0, I %% 64 == 0 and I <= 2040 (d=%d I=%d)", D.d, D.I);
-    // the tiled (prefill) path: bf16, 128-position blocks, d % 256, I % 128
+    // the tiled (prefill) path: bf16, 256-position blocks, d % 256, I % 128
     const bool gemm_ok = D.dtype == BEAM_BF16 && D.d % 256 == 0 && D.I % 128 == 0 &&
-                         (D.block_m == 0 || D.block_m == 128);
+                         (D.block_m == 0 || D.block_m == 256);
     if ((D.flags & BEAM_FORCE_PREFILL) && !gemm_ok)
         return fail(BEAM_EUNSUPPORTED,
-                    "the tiled path needs bf16, d %% 256 == 0, I %% 128 == 0, block_m 0 or 128");
+                    "the tiled path needs bf16, d %% 256 == 0, I %% 128 == 0, block_m 0 or 256");
     const long long TK = (long long)D.T * D.K;
     if (TK > (1ll << 30)) return fail(BEAM_EUNSUPPORTED, "T*K=%lld too large", TK);
 
@@ -73,7 +74,7 @@ int make_plan(const beam_moe_desc *desc, Plan &p) {
                      (!(D.flags & BEAM_FORCE_DECODE) && gemm_ok && D.T > 512)
                  ? 1
                  : 0;
-    p.bm = p.path == 1 ? 128 : (D.block_m ? D.block_m : 16);
+    p.bm = p.path == 1 ? 256 : (D.block_m ? D.block_m : 16);
     const float tau = D.tau == 0.f ? 0.5f : D.tau;
     // m = [sigmoid(z) >= tau]  <=>  z >= ln(tau / (1 - tau)); exactly 0 at tau = 0.5
     p.thr = tau == 0.5f ? 0.f : (float)std::log((double)tau / (1.0 - (double)tau));

@@ -370,7 +370,11 @@ static void launch_select_l(const Plan &p, const Routing &r, const Work &w, hipS
 
 hipError_t launch_route(const Plan &p, const void *x, const void *Wg, const void *Wm,
                         const Routing &r, const Work &w, hipStream_t s) {
-    if (p.dtype == 1) {
+    if (p.dtype == 1 && p.path == 1) {
+        // large batch: the logits as one dense MFMA GEMM
+        hipError_t err = launch_gemm_router(p, x, Wg, Wm, r, s);
+        if (err != hipSuccess) return err;
+    } else if (p.dtype == 1) {
         // few tokens: 16-token router tiles; more: 32-token tiles
         const int mt = p.T <= 16 ? 1 : 2;
         const dim3 grid((p.T + 16 * mt - 1) / (16 * mt), (2 * p.E + 15) / 16);

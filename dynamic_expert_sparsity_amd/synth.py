@@ -39,7 +39,8 @@ from dataclasses import dataclass
 
 import torch
 
-__all__ = ["LayerShape", "SHAPES", "make_layer", "workload_name"]
+__all__ = ["LayerShape", "SHAPES", "make_layer", "make_tokens", "with_mask_bias",
+           "workload_name"]
 
 
 @dataclass(frozen=True)
@@ -149,6 +150,25 @@ def make_layer(shape: LayerShape | str, T: int, *, seed: int = 0, layer: int = 0
                               _gen(dev, seed, layer, _TID["Ws_dt"], s))
         out["Ws_gu"] = Ws_gu
         out["Ws_dt"] = Ws_dt
+    return out
+
+
+def make_tokens(shape: LayerShape | str, T: int, *, seed: int = 0, layer: int = 0,
+                device="cpu") -> torch.Tensor:
+    """x [T, d] of make_layer's recipe (N(0,1), channel 0 = 1) on its own stream."""
+    if isinstance(shape, str):
+        shape = SHAPES[shape]
+    dev = torch.device(device)
+    x = _randn((T, shape.d), 1.0, torch.float32, dev, _gen(dev, seed, layer, _TID["x"], 1))
+    if T > 0:
+        x[:, 0] = 1.0
+    return x.to(shape.dtype)
+
+
+def with_mask_bias(W_mask: torch.Tensor, b: float) -> torch.Tensor:
+    """A copy of W_mask with its input-channel-0 column set to the bias b."""
+    out = W_mask.clone()
+    out[:, 0] = float(b)
     return out
 
 

@@ -61,7 +61,10 @@ extern "C" {
 
 /* desc.flags */
 #define BEAM_FORCE_DECODE   (1u << 0) /* weight-streaming expert kernels          */
-#define BEAM_FORCE_PREFILL  (1u << 1) /* LDS-tiled grouped-GEMM expert kernels     */
+#define BEAM_FORCE_PREFILL  (1u << 1) /* LDS-tiled grouped-GEMM expert kernels;
+                                         bf16, d % 256 == 0, I % 128 == 0.
+                                         Without a flag the library takes the
+                                         tiled path for T > 512 where allowed */
 
 /* stage ids for the optional per-stage events of beam_moe_forward_ex */
 #define BEAM_STAGE_ROUTER   0 /* a1-a4: router logits, top-K, softmax, mask,
@@ -81,7 +84,8 @@ typedef struct beam_moe_desc {
     int32_t  K;        /* top-K                                    (1..E)      */
     int32_t  I;        /* expert intermediate size                 (> 0)       */
     int32_t  dtype;    /* BEAM_F32 or BEAM_BF16                                */
-    int32_t  block_m;  /* 0 = library picks; else 16, 32, 64 or 128            */
+    int32_t  block_m;  /* 0 = library picks (16 streaming, 256 tiled); else
+                          16, 32, 64, 128 or 256 (the tiled path: 256 only)   */
     uint32_t flags;    /* BEAM_FORCE_*                                         */
     float    tau;      /* mask threshold on sigmoid(z); 0 means 0.5 (Eq. 6).
                           Evaluated exactly as z >= ln(tau / (1 - tau)).       */

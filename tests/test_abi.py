@@ -47,7 +47,7 @@ def test_version_and_strerror():
 def test_query_sizes(T, d, E, K, I, dt):
     s = B.query(B.make_desc(T, d, E, K, I, dt))
     bm = s["block_m"]
-    assert bm in (16, 32, 64, 128)
+    assert bm in (16, 32, 64, 128, 256)
     # capacity bound: every active pair plus at most bm-1 pads per non-empty expert
     assert s["cap"] >= T * K + min(E, T * K) * (bm - 1)
     assert s["cap"] % bm == 0 and s["n_blocks_cap"] == s["cap"] // bm
@@ -63,6 +63,8 @@ def test_query_sizes(T, d, E, K, I, dt):
     (dict(flags=3), B.BEAM_EINVAL), (dict(tau=1.5), B.BEAM_EINVAL),
     (dict(E=300), B.BEAM_EUNSUPPORTED), (dict(d=100), B.BEAM_EUNSUPPORTED),
     (dict(I=48), B.BEAM_EUNSUPPORTED),
+    (dict(I=128, flags=2, block_m=128), B.BEAM_EUNSUPPORTED),
+    (dict(I=64, flags=2), B.BEAM_EUNSUPPORTED),
 ])
 def test_query_rejects(kw, code):
     a = dict(T=4, d=256, E=16, K=2, I=64, dtype=1, block_m=0, flags=0, tau=0.0)
@@ -71,6 +73,18 @@ def test_query_rejects(kw, code):
         B.query(B.make_desc(**a))
     assert ei.value.status == code
     assert B.lib().beam_moe_last_error()
+
+
+def test_path_choice():
+    # streaming path up to 512 tokens, tiled path (256-position blocks) above
+    assert B.query(B.make_desc(512, 2048, 128, 8, 768, 1))["path"] == 0
+    s = B.query(B.make_desc(513, 2048, 128, 8, 768, 1))
+    assert s["path"] == 1 and s["block_m"] == 256
+    # float32 layers and forced decode stay on the streaming path
+    assert B.query(B.make_desc(4096, 256, 16, 2, 128, 0))["path"] == 0
+    assert B.query(B.make_desc(4096, 2048, 128, 8, 768, 1, flags=1))["path"] == 0
+    s = B.query(B.make_desc(4, 256, 16, 2, 128, 1, flags=2, block_m=256))
+    assert s["path"] == 1 and s["block_m"] == 256
 
 
 def test_reserved_must_be_zero():

@@ -95,7 +95,7 @@ def test_zero_tokens():
     assert y.shape == (0, 128)
 
 
-# ---- the tiled (prefill) path: grouped MFMA GEMMs over 128-position blocks --
+# ---- the tiled (prefill) path: grouped MFMA GEMMs over 256-position blocks --
 GEMM_SMALL = synth.LayerShape(256, 8, 2, 128, torch.bfloat16)
 
 
@@ -112,7 +112,7 @@ def test_prefill_and_decode_paths_agree():
     L = layer("qwen3", 600, seed=1100, mask_bias=0.0)
     yd, Rd, _ = run(L, 8, flags=B.BEAM_FORCE_DECODE)
     yp, Rp, lay = run(L, 8, flags=B.BEAM_FORCE_PREFILL)
-    assert lay.sizes["path"] == 1 and lay.sizes["block_m"] == 128
+    assert lay.sizes["path"] == 1 and lay.sizes["block_m"] == 256
     np.testing.assert_array_equal(Rd["masked_ids"].numpy(), Rp["masked_ids"].numpy())
     err = np.linalg.norm(yd - yp) / np.linalg.norm(yp)
     assert err < 5e-3
