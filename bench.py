@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--prefill-biases", default="-1.04,-0.52,0,8",
                     help="mask biases of the prefill runs (keep rate Phi(b))")
+    ap.add_argument("--prefill-flags", type=int, default=0,
+                    help="descriptor flags of the prefill runs (1 forces the streaming path, "
+                         "2 the tiled path; 0 lets the library choose)")
     ap.add_argument("--only-prefill", action="store_true",
                     help="measure the prefill runs only (no decode headline, sweep or CPU baseline)")
     ap.add_argument("--skew", action="store_true", default=True,
@@ -235,12 +238,12 @@ def main():
             S = sets[s]
             if skew:
                 Sk = synth.make_layer(shape, T, seed=1, layer=100 + s, skew=True, device=dev)
-                Ls.append((B.MoELayer(Sk["W_gate"], Sk["W_mask"], Sk["W_gu"], Sk["W_dt"], K),
-                           Sk["x"]))
+                Ls.append((B.MoELayer(Sk["W_gate"], Sk["W_mask"], Sk["W_gu"], Sk["W_dt"], K,
+                                      flags=args.prefill_flags), Sk["x"]))
             else:
                 x = synth.make_tokens(shape, T, seed=0, layer=s, device=dev)
                 Ls.append((B.MoELayer(S["W_gate"], synth.with_mask_bias(S["W_mask"], b),
-                                      S["W_gu"], S["W_dt"], K), x))
+                                      S["W_gu"], S["W_dt"], K, flags=args.prefill_flags), x))
         ms, _ = timed(Ls, steps, 3)
         kern = {k: timed(Ls, steps, 2, events=k)[1][k] for k in ("router", "up", "down")}
         cs = counts(Ls)

@@ -2,6 +2,7 @@
 // carve-up and the stage sequence (declared in include/beam_moe.h).
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -75,6 +76,9 @@ int make_plan(const beam_moe_desc *desc, Plan &p) {
                  ? 1
                  : 0;
     p.bm = p.path == 1 ? 256 : (D.block_m ? D.block_m : 16);
+    // below ~40 active pairs per expert the weights stream faster through the
+    // streaming kernels than through mostly empty 256-row GEMM tiles
+    p.split = p.path == 1 ? ((D.flags & BEAM_FORCE_PREFILL) ? 0 : 40) : INT_MAX;
     const float tau = D.tau == 0.f ? 0.5f : D.tau;
     // m = [sigmoid(z) >= tau]  <=>  z >= ln(tau / (1 - tau)); exactly 0 at tau = 0.5
     p.thr = tau == 0.5f ? 0.f : (float)std::log((double)tau / (1.0 - (double)tau));
@@ -92,7 +96,7 @@ int make_plan(const beam_moe_desc *desc, Plan &p) {
     p.off_tile_mask = off; off = align_up(off + (size_t)p.n_tiles * D.E * 8, 256);
     p.off_tile_base = off; off = align_up(off + (size_t)p.n_tiles * D.E * 4, 256);
     p.off_pair_pos = off;  off = align_up(off + (size_t)TK * 4, 256);
-    p.off_meta = off;      off = align_up(off + (size_t)D.E * 16, 256);
+    p.off_meta = off;      off = align_up(off + (size_t)(D.E + 1) * 16, 256);
     p.off_stok = off;      off = align_up(off + (size_t)p.cap * 4, 256);
     p.route_bytes = off;
     p.off_h = off;         off = align_up(off + (size_t)p.cap * D.I * elt, 256);

@@ -12,6 +12,8 @@
 //   offsets[e] + (pairs of e in earlier tiles) + rank,
 // which lists each expert's pairs in ascending pair id with no atomics.
 #pragma once
+#include <climits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -34,9 +36,10 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 // ascending order followed by zero records, which the expert kernels start
 // from (count 0: nothing to do).
 __device__ __forceinline__ void offsets_from_counts(const int *s_cnt, int *s_off, int E, int bm,
-                                                    const Routing &r, int32_t *meta, int lane) {
+                                                    const Routing &r, int32_t *meta, int split,
+                                                    int lane) {
     int c[4], pad[4], act[4];
-    int sc = 0, sp = 0, sa = 0;
+    int sc = 0, sp = 0, sa = 0, mx = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int ex = lane * 4 + j;
@@ -46,7 +49,10 @@ __device__ __forceinline__ void offsets_from_counts(const int *s_cnt, int *s_off
         sc += c[j];
         sp += pad[j];
         sa += act[j];
+        mx = max(mx, c[j]);
     }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o));
     const int ic = wave_incl_scan(sc, lane);
     const int ip = wave_incl_scan(sp, lane);
     const int ia = wave_incl_scan(sa, lane);
@@ -77,11 +83,17 @@ __device__ __forceinline__ void offsets_from_counts(const int *s_cnt, int *s_off
         r.num_active[1] = ip;
         r.num_active[2] = ia;
         r.num_active[3] = ip / bm;
+        // expert kernels for this call (Plan::split)
+        const int mode = split == 0 ? 1
+                         : split == INT_MAX ? 0
+                         : (ic >= split * ia || mx > 4 * split) ? 1 : 0;
+        *reinterpret_cast<int4 *>(meta + 4 * E) = make_int4(mode, mx, 0, 0);
     }
 }
 
-// All threads: block -> expert map and the pad entries of every expert's
-// segment (sorted pair TK, token 0), one thread per block of bm slots.
+// All threads: block -> expert map (one thread per block) and the pad entries
+// of every expert's segment (sorted pair TK, token 0; one wave per expert, its
+// lanes over the pad slots, so the stores coalesce).
 __device__ __forceinline__ void blocks_and_pads(const int *s_off, const int *s_cnt, int E, int bm,
                                                 int TK, const Routing &r, int32_t *sorted_tok,
                                                 int tid, int nthreads) {
@@ -94,8 +106,11 @@ __device__ __forceinline__ void blocks_and_pads(const int *s_off, const int *s_c
             if (s_off[mid] <= pos) lo = mid; else hi = mid - 1;
         }
         r.block_expert[b] = lo;
-        const int end_valid = s_off[lo] + s_cnt[lo];
-        for (int q = max(pos, end_valid); q < pos + bm; ++q) {
+    }
+    const int lane = tid & 63, nw = nthreads >> 6;
+    for (int e = tid >> 6; e < E; e += nw) {
+        const int end = s_off[e + 1];
+        for (int q = s_off[e] + s_cnt[e] + lane; q < end; q += 64) {
             r.sorted_pairs[q] = TK;
             sorted_tok[q] = 0;
         }
@@ -134,8 +149,8 @@ __device__ __forceinline__ void scatter_pair(int p, int K, int E, const Routing 
 __device__ __forceinline__ void scan_tiles(const uint64_t *tile_mask, int n_tiles, int E, int bm,
                                            int K, int TK, const Routing &r, int32_t *tile_base,
                                            int32_t *pair_pos, int32_t *meta, int32_t *sorted_tok,
-                                           bool do_scatter, int tid, int nthreads, int *s_part,
-                                           int *s_cnt, int *s_off) {
+                                           bool do_scatter, int split, int tid, int nthreads,
+                                           int *s_part, int *s_cnt, int *s_off) {
     const int NG = nthreads / E;
     const int g = tid / E;
     const int e = tid - g * E;
@@ -163,7 +178,7 @@ __device__ __forceinline__ void scan_tiles(const uint64_t *tile_mask, int n_tile
         if (g == 0) s_cnt[e] = total;
     }
     __syncthreads();
-    if (tid < 64) offsets_from_counts(s_cnt, s_off, E, bm, r, meta, tid);
+    if (tid < 64) offsets_from_counts(s_cnt, s_off, E, bm, r, meta, split, tid);
     __syncthreads();
     blocks_and_pads(s_off, s_cnt, E, bm, TK, r, sorted_tok, tid, nthreads);
     if (do_scatter)

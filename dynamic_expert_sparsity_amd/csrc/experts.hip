@@ -77,7 +77,10 @@ template <int NW, int NK>
 __global__ __launch_bounds__(NW * 64) void up_stream_bf16(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ Wgu,
     const int32_t *__restrict__ meta, const int32_t *__restrict__ num_active,
-    const int32_t *__restrict__ sorted_tok, bf16_t *__restrict__ h, int d, int I) {
+    const int32_t *__restrict__ sorted_tok, bf16_t *__restrict__ h, int d, int I,
+    const int32_t *__restrict__ mode) {
+    // mode: NULL, or the per-call choice (1: this call's experts take the tiled kernels)
+    if (mode != nullptr && *mode == 1) return;
     const int ncg = I >> 4;
     const int ai = blockIdx.x / ncg;
     const int cg = blockIdx.x - ai * ncg;
@@ -161,7 +164,8 @@ template <int NK>
 __global__ __launch_bounds__(256) void down_stream_bf16(
     const bf16_t *__restrict__ Wdt, const bf16_t *__restrict__ h,
     const int32_t *__restrict__ meta, const int32_t *__restrict__ num_active,
-    bf16_t *__restrict__ o, int d, int I) {
+    bf16_t *__restrict__ o, int d, int I, const int32_t *__restrict__ mode) {
+    if (mode != nullptr && *mode == 1) return;
     extern __shared__ __align__(16) unsigned char lds_raw[];
     bf16_t *hs = reinterpret_cast<bf16_t *>(lds_raw);
     const int pitch = I + 8;
@@ -306,13 +310,18 @@ __global__ __launch_bounds__(256) void combine_bf16(const bf16_t *__restrict__ o
 
 hipError_t launch_expert_up(const Plan &p, const void *x, const void *W_gu, const Routing &r,
                             const Work &w, hipStream_t s) {
-    if (p.path == 1) return launch_gemm_up(p, x, W_gu, r, w, s);
+    if (p.path == 1) {
+        // tiled GEMM, then the streaming kernels; the per-call mode record
+        // lets exactly one of them work (only the GEMM when split == 0)
+        const hipError_t e = launch_gemm_up(p, x, W_gu, r, w, s);
+        if (e != hipSuccess || p.split == 0) return e;
+    }
     if (p.dtype == 1) {
         const unsigned grid = (unsigned)p.max_active * (unsigned)(p.I / 16);
 #define BEAM_UP(NWV, NKV)                                                                     \
     up_stream_bf16<NWV, NKV><<<grid, NWV * 64, 0, s>>>(                                      \
         (const bf16_t *)x, (const bf16_t *)W_gu, w.meta, r.num_active, w.sorted_tok,          \
-        (bf16_t *)w.h, p.d, p.I)
+        (bf16_t *)w.h, p.d, p.I, p.path == 1 ? w.meta + 4 * p.E : nullptr)
         if (p.d % 256 == 0) {  // eight waves split d, d / 256 k-steps each
             switch (p.d / 256) {
                 case 1: BEAM_UP(8, 1); break;
@@ -338,14 +347,17 @@ hipError_t launch_expert_up(const Plan &p, const void *x, const void *W_gu, cons
 
 hipError_t launch_expert_down(const Plan &p, const void *W_dt, const Routing &r, const Work &w,
                               hipStream_t s) {
-    if (p.path == 1) return launch_gemm_down(p, W_dt, r, w, s);
+    if (p.path == 1) {
+        const hipError_t e = launch_gemm_down(p, W_dt, r, w, s);
+        if (e != hipSuccess || p.split == 0) return e;
+    }
     if (p.dtype == 1) {
         const unsigned grid = (unsigned)p.max_active * (unsigned)(p.d / 64);
         const size_t lds = (size_t)16 * (p.I + 8) * sizeof(bf16_t);
 #define BEAM_DOWN(NKV)                                                                        \
     down_stream_bf16<NKV><<<grid, 256, lds, s>>>((const bf16_t *)W_dt, (const bf16_t *)w.h,   \
                                                  w.meta, r.num_active, (bf16_t *)w.o, p.d,    \
-                                                 p.I)
+                                                 p.I, p.path == 1 ? w.meta + 4 * p.E : nullptr)
         switch (p.I / 32) {  // k-steps per wave
             case 2: BEAM_DOWN(2); break;
             case 4: BEAM_DOWN(4); break;

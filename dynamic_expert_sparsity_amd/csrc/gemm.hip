@@ -139,6 +139,7 @@ struct GemmArgs {
     int T, d, I, E;
     int n_ntiles;           // column tiles per block
     int n_rblocks;          // ROUTER: row blocks
+    const int32_t *mode;    // UP/DOWN: NULL, or the per-call choice (0: streaming kernels)
 };
 
 template <int MODE, int BM, int NA, int NB, int DKK>
@@ -154,6 +155,8 @@ __global__ __launch_bounds__(BM * 2, 1) void grouped_gemm(GemmArgs g) {
     const int lr = lane & 31;
     const int lh = lane >> 5;
 
+    // this call's experts go to the streaming kernels
+    if (MODE != MODE_ROUTER && g.mode != nullptr && *g.mode == 0) return;
     const int n_blocks = MODE == MODE_ROUTER ? g.n_rblocks : g.num_active[3];
     const int n_tiles = n_blocks * g.n_ntiles;
     const int xcd = blockIdx.x & 7;
@@ -392,6 +395,7 @@ static GemmArgs base_args(const Plan &p, const Routing &r, const Work &w) {
     a.sorted_tok = w.sorted_tok;
     a.expert_offsets = r.expert_offsets;
     a.expert_counts = r.expert_counts;
+    a.mode = p.split == 0 ? nullptr : w.meta + 4 * p.E;
     a.T = p.T;
     a.d = p.d;
     a.I = p.I;

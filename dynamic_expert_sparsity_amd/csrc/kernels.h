@@ -12,6 +12,10 @@ struct Plan {
     int dtype;          // 0 f32, 1 bf16
     int bm;             // block_m
     int path;           // 0 streaming (decode), 1 tiled (prefill)
+    int split;          // INT_MAX: streaming kernels only; 0: tiled kernels only;
+                        // else chosen per call on the device: tiled if the active
+                        // pairs average >= split per active expert or one expert
+                        // has more than 4 * split (the mode record after meta)
     float thr;          // mask logit threshold: m = [z >= thr]
     // select / compaction
     int s_ts;           // tokens per select tile (64)
@@ -40,7 +44,8 @@ struct Work {  // workspace views
     uint64_t *tile_mask;
     int32_t *tile_base;
     int32_t *pair_pos;   // [T*K] sorted position of each pair, -1 if masked
-    int32_t *meta;       // [E][4] per active expert: {expert, offset, count, 0}
+    int32_t *meta;       // [E][4] per active expert: {expert, offset, count, 0},
+                         // then {mode (1 tiled, 0 streaming), max count, 0, 0}
     int32_t *sorted_tok; // [cap] token of each sorted position (pads: unset)
     void *h;
     void *o;

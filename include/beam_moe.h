@@ -63,8 +63,12 @@ extern "C" {
 #define BEAM_FORCE_DECODE   (1u << 0) /* weight-streaming expert kernels          */
 #define BEAM_FORCE_PREFILL  (1u << 1) /* LDS-tiled grouped-GEMM expert kernels;
                                          bf16, d % 256 == 0, I % 128 == 0.
-                                         Without a flag the library takes the
-                                         tiled path for T > 512 where allowed */
+                                         Without a flag, where allowed and
+                                         T > 512, the device picks per call from
+                                         the routed counts: tiled kernels if the
+                                         active pairs average >= 40 per active
+                                         expert or one expert has > 160, else
+                                         the streaming kernels                 */
 
 /* stage ids for the optional per-stage events of beam_moe_forward_ex */
 #define BEAM_STAGE_ROUTER   0 /* a1-a4: router logits, top-K, softmax, mask,
@@ -122,7 +126,9 @@ typedef struct beam_moe_sizes {
     int64_t cap;               /* length of sorted_pairs                        */
     int64_t n_blocks_cap;      /* length of block_expert                        */
     int32_t block_m;           /* block size in effect                          */
-    int32_t path;              /* 0 = decode (streaming), 1 = prefill (tiled)   */
+    int32_t path;              /* 0 = streaming kernels; 1 = tiled kernels (or,
+                                  without BEAM_FORCE_PREFILL, streaming ones
+                                  when the device finds few pairs per expert) */
 } beam_moe_sizes;
 
 /* beam_moe_query: validate `desc` and fill `out`.

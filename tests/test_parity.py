@@ -118,6 +118,27 @@ def test_prefill_and_decode_paths_agree():
     assert err < 5e-3
 
 
+# ---- default above 512 tokens: the device picks, per call, the tiled kernels
+# (active pairs average >= 40 per active expert, or one expert above 160) or
+# the streaming kernels; skewed routing at E=16 lands on the tiled side (one
+# expert above 160), at E=32 on the streaming side
+def _expects_tiled(counts):
+    act = counts[counts > 0]
+    return counts.sum() >= 40 * len(act) or counts.max() > 160
+
+
+@pytest.mark.parametrize("E,tiled", [(16, True), (32, False)])
+def test_per_call_kernel_choice(E, tiled):
+    import dynamic_expert_sparsity_amd as B
+    shape = synth.LayerShape(256, E, 2, 128, torch.bfloat16)
+    L = layer(shape, 900, seed=1500, skew=True)
+    y, G, O, _ = _full_check(L, 2)
+    assert _expects_tiled(G["counts"]) == tiled
+    lay = B.MoELayer(L["W_gate"], L["W_mask"], L["W_gu"], L["W_dt"], 2)
+    lay(L["x"])
+    assert lay.sizes["path"] == 1 and lay.sizes["block_m"] == 256
+
+
 @pytest.mark.parametrize("b", [0.0, 8.0])
 def test_qwen3_prefill_8192(b):
     L = layer("qwen3", 8192, seed=1200, mask_bias=b)
