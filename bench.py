@@ -154,6 +154,8 @@ def main():
         launch stream, averaged over the steps (the kernel's launch duration).
         Returns (ms per step, dict of per-stage ms per step or None)."""
         ns = len(Ls)
+        for lay, x in Ls:  # buffers of every layer allocated before any timing
+            lay.prepare(x.shape[0])
         for i in range(warmup):
             lay, x = Ls[i % ns]
             lay(x)

@@ -228,6 +228,11 @@ class MoELayer:
         self.block_m, self.flags, self.tau = block_m, flags, tau
         self._T = None
 
+    def prepare(self, T):
+        """Allocate the output, routing and workspace buffers for T tokens
+        (done by the first call with that T otherwise)."""
+        self._prepare(T)
+
     def _prepare(self, T):
         if self._T == T:
             return
