@@ -97,7 +97,10 @@ int make_plan(const beam_moe_desc *desc, Plan &p) {
     p.off_tile_base = off; off = align_up(off + (size_t)p.n_tiles * D.E * 4, 256);
     p.off_pair_pos = off;  off = align_up(off + (size_t)TK * 4, 256);
     p.off_meta = off;      off = align_up(off + (size_t)(D.E + 1) * 16, 256);
-    p.off_stok = off;      off = align_up(off + (size_t)p.cap * 4, 256);
+    // position blocks of <= 32: at most one partial block per active expert
+    p.off_pbt = off;       off = align_up(off + (size_t)(p.max_active + TK / 32 + 1) * 16, 256);
+    // sorted tokens, plus 32 slack entries read (not used) past a block end
+    p.off_stok = off;      off = align_up(off + (size_t)(p.cap + 32) * 4, 256);
     p.route_bytes = off;
     p.off_h = off;         off = align_up(off + (size_t)p.cap * D.I * elt, 256);
     p.off_o = off;         off = align_up(off + (size_t)p.cap * D.d * elt, 256);
@@ -132,6 +135,7 @@ Work carve(const Plan &p, void *ws) {
     w.tile_base = reinterpret_cast<int32_t *>(b + p.off_tile_base);
     w.pair_pos = reinterpret_cast<int32_t *>(b + p.off_pair_pos);
     w.meta = reinterpret_cast<int32_t *>(b + p.off_meta);
+    w.pbt = reinterpret_cast<int32_t *>(b + p.off_pbt);
     w.sorted_tok = reinterpret_cast<int32_t *>(b + p.off_stok);
     w.h = b + p.off_h;
     w.o = b + p.off_o;

@@ -34,21 +34,25 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 // r.num_active = {P, num_padded, n_active_experts, n_blocks}, and the E
 // records meta[i] = {expert, offset, count, 0} of the active experts in
 // ascending order followed by zero records, which the expert kernels start
-// from (count 0: nothing to do).
+// from (count 0: nothing to do), the call's record meta[E] = {mode, max count,
+// position blocks, 0}, and one record {expert, first position, rows, 0} per
+// block of up to 32 consecutive positions of an expert (pbt, in expert order).
 __device__ __forceinline__ void offsets_from_counts(const int *s_cnt, int *s_off, int E, int bm,
-                                                    const Routing &r, int32_t *meta, int split,
-                                                    int lane) {
-    int c[4], pad[4], act[4];
-    int sc = 0, sp = 0, sa = 0, mx = 0;
+                                                    const Routing &r, int32_t *meta,
+                                                    int32_t *pbt, int split, int lane) {
+    int c[4], pad[4], act[4], npb[4];
+    int sc = 0, sp = 0, sa = 0, mx = 0, sb = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int ex = lane * 4 + j;
         c[j] = ex < E ? s_cnt[ex] : 0;
         pad[j] = (c[j] + bm - 1) / bm * bm;
         act[j] = c[j] > 0 ? 1 : 0;
+        npb[j] = (c[j] + 31) >> 5;
         sc += c[j];
         sp += pad[j];
         sa += act[j];
+        sb += npb[j];
         mx = max(mx, c[j]);
     }
 #pragma unroll
@@ -56,7 +60,14 @@ __device__ __forceinline__ void offsets_from_counts(const int *s_cnt, int *s_off
     const int ic = wave_incl_scan(sc, lane);
     const int ip = wave_incl_scan(sp, lane);
     const int ia = wave_incl_scan(sa, lane);
-    int op = ip - sp, oa = ia - sa;
+    const int ib = wave_incl_scan(sb, lane);
+    int op = ip - sp, oa = ia - sa, ob = ib - sb;
+    // expert kernels for this call (Plan::split); the block records are only
+    // read by the streaming kernels
+    const int tot_c = __shfl(ic, 63), tot_a = __shfl(ia, 63);
+    const int mode = split == 0 ? 1
+                     : split == INT_MAX ? 0
+                     : (tot_c >= split * tot_a || mx > 4 * split) ? 1 : 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int ex = lane * 4 + j;
@@ -68,9 +79,14 @@ __device__ __forceinline__ void offsets_from_counts(const int *s_cnt, int *s_off
                 r.active_experts[oa] = ex;
                 *reinterpret_cast<int4 *>(meta + 4 * oa) = make_int4(ex, op, c[j], 0);
             }
+            if (mode == 0)
+                for (int q = 0; q < npb[j]; ++q)
+                    *reinterpret_cast<int4 *>(pbt + 4 * (ob + q)) =
+                        make_int4(ex, op + 32 * q, min(32, c[j] - 32 * q), 0);
         }
         op += pad[j];
         oa += act[j];
+        ob += npb[j];
     }
     // slots past the active count get count 0, the expert kernels' exit test
     const int n_act = __shfl(ia, 63);
@@ -83,11 +99,7 @@ __device__ __forceinline__ void offsets_from_counts(const int *s_cnt, int *s_off
         r.num_active[1] = ip;
         r.num_active[2] = ia;
         r.num_active[3] = ip / bm;
-        // expert kernels for this call (Plan::split)
-        const int mode = split == 0 ? 1
-                         : split == INT_MAX ? 0
-                         : (ic >= split * ia || mx > 4 * split) ? 1 : 0;
-        *reinterpret_cast<int4 *>(meta + 4 * E) = make_int4(mode, mx, 0, 0);
+        *reinterpret_cast<int4 *>(meta + 4 * E) = make_int4(mode, mx, ib, 0);
     }
 }
 
@@ -149,8 +161,8 @@ __device__ __forceinline__ void scatter_pair(int p, int K, int E, const Routing 
 __device__ __forceinline__ void scan_tiles(const uint64_t *tile_mask, int n_tiles, int E, int bm,
                                            int K, int TK, const Routing &r, int32_t *tile_base,
                                            int32_t *pair_pos, int32_t *meta, int32_t *sorted_tok,
-                                           bool do_scatter, int split, int tid, int nthreads,
-                                           int *s_part, int *s_cnt, int *s_off) {
+                                           int32_t *pbt, bool do_scatter, int split, int tid,
+                                           int nthreads, int *s_part, int *s_cnt, int *s_off) {
     const int NG = nthreads / E;
     const int g = tid / E;
     const int e = tid - g * E;
@@ -178,7 +190,7 @@ __device__ __forceinline__ void scan_tiles(const uint64_t *tile_mask, int n_tile
         if (g == 0) s_cnt[e] = total;
     }
     __syncthreads();
-    if (tid < 64) offsets_from_counts(s_cnt, s_off, E, bm, r, meta, split, tid);
+    if (tid < 64) offsets_from_counts(s_cnt, s_off, E, bm, r, meta, pbt, split, tid);
     __syncthreads();
     blocks_and_pads(s_off, s_cnt, E, bm, TK, r, sorted_tok, tid, nthreads);
     if (do_scatter)

@@ -10,6 +10,8 @@
 //               layer, rounded to nearest even; float for the float layer)
 //   o [cap, d]  expert output per sorted position (same element type)
 // and the combine reads o through pair_pos[t*K + k] (-1 when masked).
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -117,13 +119,21 @@ __global__ __launch_bounds__(NW * 64) void up_stream_bf16(
             const int v = st[j];
             tok = li == j ? v : tok;
         }
-        tok = pc + li < cnt ? tok : 0;
+        // positions past the count: zero operands, no load (a decode expert
+        // has a few tokens, so most of the 16 rows are such pads)
+        const bool have = pc + li < cnt;
+        tok = have ? tok : 0;
         const bf16_t *xa = x + (size_t)tok * d + kb + kq;
         f32x4 ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
         if constexpr (NK > 0) {
             __builtin_amdgcn_sched_barrier(0);
+            if (have) {
 #pragma unroll
-            for (int k = 0; k < NK; ++k) rx[k] = ld16(xa + 32 * k);
+                for (int k = 0; k < NK; ++k) rx[k] = ld16(xa + 32 * k);
+            } else {
+#pragma unroll
+                for (int k = 0; k < NK; ++k) rx[k] = u32x4{0u, 0u, 0u, 0u};
+            }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int k = 0; k < NK; ++k) {
@@ -186,12 +196,13 @@ __global__ __launch_bounds__(256) void down_stream_bf16(
     const int chunks = I >> 3;  // 16-byte chunks per row
 
     for (int pc = 0; pc < cnt; pc += 16) {
-        // rows past cnt are the padded segment's rows (inside the buffer);
-        // their results land in D rows that are not stored
+        // rows past the count are zero-filled, not loaded (a decode expert
+        // has a few tokens); their results land in D rows that are not stored
+        const int nrow = min(16, cnt - pc);
         for (int q = tid; q < 16 * chunks; q += 256) {
             const int row = q / chunks, ch = q - row * chunks;
             *reinterpret_cast<u32x4 *>(hs + row * pitch + ch * 8) =
-                ld16(h + (size_t)(off + pc + row) * I + ch * 8);
+                row < nrow ? ld16(h + (size_t)(off + pc + row) * I + ch * 8) : u32x4{0u, 0u, 0u, 0u};
         }
         __syncthreads();
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -308,6 +319,265 @@ __global__ __launch_bounds__(256) void combine_bf16(const bf16_t *__restrict__ o
     }
 }
 
+// ---------------------------------------------------------------------------
+// Up and down projections, ring-streamed (bf16, k length % 256 == 0).  A
+// unit is (block of up to 32 positions of one expert, column group): 32 rows
+// of the expert's weights (up: 16 gate + 16 up rows; down: 32 output
+// channels).  A persistent grid of one 8-wave workgroup per CU walks a
+// contiguous range of units, streaming them through RING_NS LDS slots in
+// k-chunks of 256 with RING_NS - 1 chunks in flight, so the reduction that
+// ends a unit overlaps the loads of the next.  A slot holds the chunk's 32
+// weight rows (512 B each, 16-byte piece c of row r at c ^ (r % 16)) and, per
+// wave, that wave's 32-wide k-slice of the block's x rows (64 B each, piece
+// c of position p at c ^ ((p / 4) % 4)): every operand arrives through
+// global_load_lds (weights non-temporal: read once), so the MFMAs read only
+// LDS and the compiler tracks no in-flight register loads.  Waits are
+// explicit vmcnt counts per wave: a chunk is 2 weight loads and 1 or 2 x
+// loads; the h stores that end a unit are not counted, which only makes the
+// next waits stricter.
+// ---------------------------------------------------------------------------
+constexpr int RING_NS = 4;                         // LDS slots
+constexpr int RING_W = 32 * 512;                   // weight rows of a slot
+constexpr int RING_X = 8 * 2 * 1024;               // x: 8 waves x 2 blocks of 16 positions
+constexpr int RING_SLOT = RING_W + RING_X;         // 32 KB
+constexpr int RING_LDS = RING_NS * RING_SLOT + 8 * 4 * 64 * 16;  // + partial sums (160 KB)
+
+template <int N>
+__device__ __forceinline__ void ring_wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 0x3) << 14));
+}
+// at most n vector-memory operations of this wave in flight (n a sum of up to
+// two chunks of 3 or 4)
+__device__ __forceinline__ void ring_wait_le(int n) {
+    if (n >= 8) ring_wait_vm<8>();
+    else if (n >= 7) ring_wait_vm<7>();
+    else if (n >= 6) ring_wait_vm<6>();
+    else if (n >= 4) ring_wait_vm<4>();
+    else if (n >= 3) ring_wait_vm<3>();
+    else ring_wait_vm<0>();
+}
+__device__ __forceinline__ void ring_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+template <int AUX>
+__device__ __forceinline__ void ring_dma(const void *g, unsigned char *l) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)l, 16, 0, AUX);
+}
+
+// DOWN = false: up projection (A = x rows of the block's tokens, B = the 16
+// gate and 16 up rows of a column group of 16 units; out h = SiLU(a) * u).
+// DOWN = true: down projection (A = the block's h rows, B = 32 rows of W_dt,
+// one per output channel of a column group of 32; out o).  klen = d (up) or
+// I (down), a multiple of 256; ncols = I (up) or d (down).
+template <bool DOWN>
+__global__ __launch_bounds__(512, 1) void ring_bf16(
+    const bf16_t *__restrict__ A, const bf16_t *__restrict__ W,
+    const int32_t *__restrict__ pbt, const int32_t *__restrict__ mrec,
+    const int32_t *__restrict__ sorted_tok, bf16_t *__restrict__ out, int klen, int ncols,
+    int check_mode) {
+    constexpr int NS = RING_NS;
+    extern __shared__ __align__(16) unsigned char lds[];
+    f32x4 *red = reinterpret_cast<f32x4 *>(lds + NS * RING_SLOT);  // [wave][2 col blocks x 2 row blocks][lane]
+    // mrec = {mode, max count, position blocks, 0}; mode 1: the tiled kernels take this call
+    if (check_mode && mrec[0] == 1) return;
+    const int NCH = klen >> 8;                     // k-chunks of 256 per row
+    const int ncg = DOWN ? ncols >> 5 : ncols >> 4;  // column groups per position block
+    const int NU = mrec[2] * ncg;
+    const int G = gridDim.x, b = blockIdx.x;
+    const int u_begin = (int)((long long)NU * b / G);
+    const int u_end = (int)((long long)NU * (b + 1) / G);
+    if (u_end <= u_begin) return;
+    const int nch = (u_end - u_begin) * NCH;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int li = lane & 15, kg = lane >> 4;
+
+    // request side: the unit whose chunks are being loaded
+    int iu = -1, i_rows = 0, i_pos0 = 0, i_cg = 0;
+    const bf16_t *wrow0 = W, *wrow1 = W;  // this lane's two weight rows (+ chunk)
+    const bf16_t *xa0 = A, *xa1 = A;      // this lane's A source for row blocks 0 / 1 (+ chunk)
+    // per slot: this wave's vector-memory ops for the chunk in it, and, when
+    // it is the last chunk of its unit, the unit's (first position, rows,
+    // column group) for the stores (requests run up to NS - 1 chunks, which
+    // can be several units, ahead of the compute)
+    int ld[NS], spos[NS], srow[NS], scg[NS];
+
+    // weight loads: instruction i covers rows 4 wave + 2 i + {0, 1}; lane l
+    // fetches piece (l % 32) ^ (r % 16) of row r = 4 wave + 2 i + l / 32
+    const int wr0 = 4 * wave + (lane >> 5), wr1 = wr0 + 2;
+    // A loads: lane l -> position 16 blk + l / 4, piece (l % 4) ^ ((l / 16) % 4)
+    const int xp = lane >> 2;
+    const int xpiece = (lane & 3) ^ ((lane >> 4) & 3);
+    // row of the unit's 32 weight rows -> row of W[e] (up: gate rows, then up rows)
+    auto wmap = [&](int r, int cg) {
+        return DOWN ? cg * 32 + r : (r < 16 ? cg * 16 + r : ncols + cg * 16 + (r - 16));
+    };
+
+    auto issue = [&](int jj, int q) {  // chunk jj into slot q (static)
+        const int uu = jj / NCH, c = jj - uu * NCH;
+        if (uu != iu) {
+            iu = uu;
+            const int U = u_begin + uu;
+            const int pbi = U / ncg, cg = U - pbi * ncg;
+            const int4 rec = *reinterpret_cast<const int4 *>(pbt + 4 * pbi);
+            const int e = rec.x, pos0 = rec.y, rows = rec.z;
+            const size_t wrows = DOWN ? (size_t)ncols : (size_t)2 * ncols;  // rows of W[e]
+            const bf16_t *we = W + (size_t)e * wrows * klen;
+            wrow0 = we + (size_t)wmap(wr0, cg) * klen + (((lane & 31) ^ (wr0 & 15)) << 3);
+            wrow1 = we + (size_t)wmap(wr1, cg) * klen + (((lane & 31) ^ (wr1 & 15)) << 3);
+            int a0, a1;  // A rows of this lane's positions xp and 16 + xp
+            if (DOWN) {
+                a0 = pos0 + (xp < rows ? xp : 0);
+                a1 = pos0 + (16 + xp < rows ? 16 + xp : 0);
+            } else {
+                // token ids of the block's positions (scalar loads); past rows: token 0
+                const int *st = sorted_tok + pos0;
+                int t0 = st[0], t1 = st[16];
+#pragma unroll
+                for (int j = 1; j < 16; ++j) {
+                    const int v0 = st[j], v1 = st[16 + j];
+                    t0 = xp == j ? v0 : t0;
+                    t1 = xp == j ? v1 : t1;
+                }
+                a0 = xp < rows ? t0 : 0;
+                a1 = 16 + xp < rows ? t1 : 0;
+            }
+            xa0 = A + (size_t)a0 * klen + wave * 32 + xpiece * 8;
+            xa1 = A + (size_t)a1 * klen + wave * 32 + xpiece * 8;
+            i_rows = rows;
+            i_pos0 = pos0;
+            i_cg = cg;
+        }
+        if (c == NCH - 1) {
+            spos[q] = i_pos0;
+            srow[q] = i_rows;
+            scg[q] = i_cg;
+        }
+        unsigned char *sl = lds + q * RING_SLOT;
+        ring_dma<2>(wrow0 + c * 256, sl + (4 * wave) * 512);
+        ring_dma<2>(wrow1 + c * 256, sl + (4 * wave + 2) * 512);
+        unsigned char *xs = sl + RING_W + wave * 2048;
+        ring_dma<0>(xa0 + c * 256, xs);
+        if (i_rows > 16) {
+            ring_dma<0>(xa1 + c * 256, xs + 1024);
+            ld[q] = 4;
+        } else {
+            ld[q] = 3;
+        }
+    };
+
+    f32x4 c00 = {0.f, 0.f, 0.f, 0.f}, c10 = c00, c01 = c00, c11 = c00;  // [col block][row block]
+#pragma unroll
+    for (int q = 0; q < NS; ++q) ld[q] = spos[q] = srow[q] = scg[q] = 0;
+#pragma unroll
+    for (int q = 0; q < NS - 1; ++q)
+        if (q < nch) issue(q, q);
+    for (int j0 = 0; j0 < nch; j0 += NS) {
+#pragma unroll
+        for (int q = 0; q < NS; ++q) {
+            const int j = j0 + q;
+            if (j >= nch) break;
+            // chunk j landed: only the chunks requested after it may be in flight
+            int later = 0;
+#pragma unroll
+            for (int t = 1; t <= NS - 2; ++t)
+                if (j + t < nch) later += ld[(q + t) % NS];
+            ring_wait_le(later);
+            ring_barrier();  // every wave's part of chunk j is in; slot of chunk j - 1 is free
+            const bool rb1 = ld[q] == 4;
+            if (j + NS - 1 < nch) issue(j + NS - 1, (q + NS - 1) % NS);
+            // this wave's 32-wide k-slice: one k-step of 32
+            const unsigned char *sl = lds + q * RING_SLOT;
+            const int gc = 4 * wave + kg;  // 16-byte piece of the weight row
+            const u32x4 w0 = *reinterpret_cast<const u32x4 *>(sl + li * 512 + ((gc ^ li) << 4));
+            const u32x4 w1 = *reinterpret_cast<const u32x4 *>(sl + (16 + li) * 512 + ((gc ^ li) << 4));
+            const unsigned char *xs = sl + RING_W + wave * 2048;
+            const int xo = li * 64 + ((kg ^ ((li >> 2) & 3)) << 4);
+            const u32x4 a0 = *reinterpret_cast<const u32x4 *>(xs + xo);
+            c00 = mfma16x16x32(a0, w0, c00);
+            c10 = mfma16x16x32(a0, w1, c10);
+            if (rb1) {
+                const u32x4 a1 = *reinterpret_cast<const u32x4 *>(xs + 1024 + xo);
+                c01 = mfma16x16x32(a1, w0, c01);
+                c11 = mfma16x16x32(a1, w1, c11);
+            }
+            const int uu = j / NCH;
+            if (j - uu * NCH == NCH - 1) {
+                // unit done: the eight waves' partial sums meet in LDS
+                red[(wave * 4 + 0) * 64 + lane] = c00;
+                red[(wave * 4 + 1) * 64 + lane] = c10;
+                red[(wave * 4 + 2) * 64 + lane] = c01;
+                red[(wave * 4 + 3) * 64 + lane] = c11;
+                __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14));  // lgkmcnt(0)
+                ring_barrier();
+                // all 512 threads reduce: thread t -> row block t / 256, lane
+                // (t / 4) % 64 of the partials, component t % 4 (one output
+                // row), summing the eight waves in order
+                const int rows = srow[q];
+                const int tt = threadIdx.x, rb = tt >> 8, L = (tt >> 2) & 63, comp = tt & 3;
+                const float *rf = reinterpret_cast<const float *>(red);
+                if (rb == 0 || rows > 16) {
+                    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+                    for (int w = 0; w < 8; ++w) {
+                        s0 += rf[((w * 4 + 2 * rb) * 64 + L) * 4 + comp];
+                        s1 += rf[((w * 4 + 2 * rb + 1) * 64 + L) * 4 + comp];
+                    }
+                    // D layout of a 16x16 MFMA: lane L holds column L % 16, rows 4 (L / 16) + comp
+                    const int row = 16 * rb + 4 * (L >> 4) + comp;
+                    if (row < rows) {
+                        bf16_t *o = out + (size_t)(spos[q] + row) * ncols;
+                        const int cg = scg[q];
+                        if (DOWN) {
+                            o[cg * 32 + (L & 15)] = f32_to_bf16(s0);
+                            o[cg * 32 + 16 + (L & 15)] = f32_to_bf16(s1);
+                        } else {
+                            o[cg * 16 + (L & 15)] = f32_to_bf16(silu<false>(s0) * s1);
+                        }
+                    }
+                }
+                c00 = f32x4{0.f, 0.f, 0.f, 0.f};
+                c10 = c00;
+                c01 = c00;
+                c11 = c00;
+            }
+        }
+    }
+}
+
+// the ring kernels: bf16 and a k length (d for up, I for down) that is a
+// multiple of 256 (I % 16 == 0 and d % 32 == 0 then hold for the column groups)
+static bool ring_ok_up(const Plan &p) { return p.dtype == 1 && p.d % 256 == 0 && p.I % 16 == 0; }
+static bool ring_ok_down(const Plan &p) { return p.dtype == 1 && p.I % 256 == 0 && p.d % 32 == 0; }
+static int ring_grid() {
+    static int n = 0;
+    static std::once_flag once;
+    std::call_once(once, [] {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+            n = cus;
+        if (n <= 0) n = 256;
+    });
+    return n;
+}
+// 160 KB of dynamic LDS: allowed once per kernel (the attribute is per function)
+static hipError_t ring_attr(const void *fn) {
+    static std::mutex mu;
+    static const void *done[8] = {};
+    std::lock_guard<std::mutex> lk(mu);
+    for (const void *f : done)
+        if (f == fn) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, RING_LDS);
+    if (e != hipSuccess) return e;
+    for (const void *&f : done)
+        if (!f) { f = fn; break; }
+    return hipSuccess;
+}
+
 hipError_t launch_expert_up(const Plan &p, const void *x, const void *W_gu, const Routing &r,
                             const Work &w, hipStream_t s) {
     if (p.path == 1) {
@@ -316,7 +586,13 @@ hipError_t launch_expert_up(const Plan &p, const void *x, const void *W_gu, cons
         const hipError_t e = launch_gemm_up(p, x, W_gu, r, w, s);
         if (e != hipSuccess || p.split == 0) return e;
     }
-    if (p.dtype == 1) {
+    if (ring_ok_up(p)) {
+        const hipError_t e = ring_attr((const void *)ring_bf16<false>);
+        if (e != hipSuccess) return e;
+        ring_bf16<false><<<ring_grid(), 512, RING_LDS, s>>>(
+            (const bf16_t *)x, (const bf16_t *)W_gu, w.pbt, w.meta + 4 * p.E, w.sorted_tok,
+            (bf16_t *)w.h, p.d, p.I, p.path == 1 ? 1 : 0);
+    } else if (p.dtype == 1) {
         const unsigned grid = (unsigned)p.max_active * (unsigned)(p.I / 16);
 #define BEAM_UP(NWV, NKV)                                                                     \
     up_stream_bf16<NWV, NKV><<<grid, NWV * 64, 0, s>>>(                                      \
@@ -351,7 +627,13 @@ hipError_t launch_expert_down(const Plan &p, const void *W_dt, const Routing &r,
         const hipError_t e = launch_gemm_down(p, W_dt, r, w, s);
         if (e != hipSuccess || p.split == 0) return e;
     }
-    if (p.dtype == 1) {
+    if (ring_ok_down(p)) {
+        const hipError_t e = ring_attr((const void *)ring_bf16<true>);
+        if (e != hipSuccess) return e;
+        ring_bf16<true><<<ring_grid(), 512, RING_LDS, s>>>(
+            (const bf16_t *)w.h, (const bf16_t *)W_dt, w.pbt, w.meta + 4 * p.E, w.sorted_tok,
+            (bf16_t *)w.o, p.I, p.d, p.path == 1 ? 1 : 0);
+    } else if (p.dtype == 1) {
         const unsigned grid = (unsigned)p.max_active * (unsigned)(p.d / 64);
         const size_t lds = (size_t)16 * (p.I + 8) * sizeof(bf16_t);
 #define BEAM_DOWN(NKV)                                                                        \

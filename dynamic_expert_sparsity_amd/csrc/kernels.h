@@ -25,7 +25,7 @@ struct Plan {
     long long n_blocks_cap; // block_expert capacity
     int max_active;     // host upper bound on experts with >= 1 active pair
     // workspace carve-up (byte offsets) and totals
-    size_t off_tile_mask, off_tile_base, off_pair_pos, off_meta, off_stok, off_h, off_o;
+    size_t off_tile_mask, off_tile_base, off_pair_pos, off_meta, off_pbt, off_stok, off_h, off_o;
     size_t route_bytes, total_bytes;
 };
 
@@ -45,7 +45,9 @@ struct Work {  // workspace views
     int32_t *tile_base;
     int32_t *pair_pos;   // [T*K] sorted position of each pair, -1 if masked
     int32_t *meta;       // [E][4] per active expert: {expert, offset, count, 0},
-                         // then {mode (1 tiled, 0 streaming), max count, 0, 0}
+                         // then {mode (1 tiled, 0 streaming), max count, position blocks, 0}
+    int32_t *pbt;        // [pb_cap][4] per block of <= 32 positions of an expert:
+                         // {expert, first position, rows, 0}
     int32_t *sorted_tok; // [cap] token of each sorted position (pads: unset)
     void *h;
     void *o;

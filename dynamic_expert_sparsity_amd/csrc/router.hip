@@ -295,12 +295,13 @@ __global__ __launch_bounds__(1024) void compact_tiles(const uint64_t *__restrict
                                                       int32_t *__restrict__ pair_pos,
                                                       int32_t *__restrict__ meta,
                                                       int32_t *__restrict__ sorted_tok,
+                                                      int32_t *__restrict__ pbt,
                                                       int fuse_scatter, int split) {
     __shared__ int s_part[1024];
     __shared__ int s_cnt[256];
     __shared__ int s_off[257];
     scan_tiles(tile_mask, n_tiles, E, bm, K, TK, r, tile_base, pair_pos, meta, sorted_tok,
-               fuse_scatter != 0, split, threadIdx.x, 1024, s_part, s_cnt, s_off);
+               pbt, fuse_scatter != 0, split, threadIdx.x, 1024, s_part, s_cnt, s_off);
 }
 
 // A small batch (T <= 64, one tile) in one workgroup: select, counts,
@@ -309,7 +310,8 @@ template <int EJ, int LPT>
 __global__ __launch_bounds__(1024) void route_small(int T, int E, int K, float thr, int bm,
                                                     Routing r, int32_t *__restrict__ pair_pos,
                                                     int32_t *__restrict__ meta,
-                                                    int32_t *__restrict__ sorted_tok, int split) {
+                                                    int32_t *__restrict__ sorted_tok,
+                                                    int32_t *__restrict__ pbt, int split) {
     __shared__ unsigned long long tmask[256];
     __shared__ int s_mid[64 * 16];
     __shared__ int s_cnt[256];
@@ -323,7 +325,7 @@ __global__ __launch_bounds__(1024) void route_small(int T, int E, int K, float t
     __syncthreads();
     if (tid < E) s_cnt[tid] = __popcll(tmask[tid]);
     __syncthreads();
-    if (tid < 64) offsets_from_counts(s_cnt, s_off, E, bm, r, meta, split, tid);
+    if (tid < 64) offsets_from_counts(s_cnt, s_off, E, bm, r, meta, pbt, split, tid);
     __syncthreads();
     const int TK = T * K;
     blocks_and_pads(s_off, s_cnt, E, bm, TK, r, sorted_tok, tid, 1024);
@@ -343,12 +345,12 @@ template <int EJ, int LPT>
 static void launch_select_t(const Plan &p, const Routing &r, const Work &w, hipStream_t s) {
     if (p.T <= 64) {
         route_small<EJ, LPT><<<1, 1024, 0, s>>>(p.T, p.E, p.K, p.thr, p.bm, r, w.pair_pos, w.meta,
-                                               w.sorted_tok, p.split);
+                                               w.sorted_tok, w.pbt, p.split);
     } else {
         select_topk_mask<EJ, LPT><<<p.n_tiles, LPT * 64, 0, s>>>(p.T, p.E, p.K, p.thr, r,
                                                                w.tile_mask);
         compact_tiles<<<1, 1024, 0, s>>>(w.tile_mask, p.n_tiles, p.E, p.bm, p.K, p.T * p.K, r,
-                                         w.tile_base, w.pair_pos, w.meta, w.sorted_tok,
+                                         w.tile_base, w.pair_pos, w.meta, w.sorted_tok, w.pbt,
                                          p.fuse_scatter, p.split);
     }
 }
