@@ -76,9 +76,10 @@ int make_plan(const beam_moe_desc *desc, Plan &p) {
                  ? 1
                  : 0;
     p.bm = p.path == 1 ? 256 : (D.block_m ? D.block_m : 16);
-    // below ~40 active pairs per expert the weights stream faster through the
-    // streaming kernels than through mostly empty 256-row GEMM tiles
-    p.split = p.path == 1 ? ((D.flags & BEAM_FORCE_PREFILL) ? 0 : 40) : INT_MAX;
+    // with few active pairs per expert the weights stream faster through the
+    // streaming kernels than through mostly empty 256-row GEMM tiles; the
+    // device decides per call from the routed counts
+    p.split = p.path == 1 ? ((D.flags & BEAM_FORCE_PREFILL) ? 0 : 1) : INT_MAX;
     const float tau = D.tau == 0.f ? 0.5f : D.tau;
     // m = [sigmoid(z) >= tau]  <=>  z >= ln(tau / (1 - tau)); exactly 0 at tau = 0.5
     p.thr = tau == 0.5f ? 0.f : (float)std::log((double)tau / (1.0 - (double)tau));

@@ -63,11 +63,14 @@ __device__ __forceinline__ void offsets_from_counts(const int *s_cnt, int *s_off
     const int ib = wave_incl_scan(sb, lane);
     int op = ip - sp, oa = ia - sa, ob = ib - sb;
     // expert kernels for this call (Plan::split); the block records are only
-    // read by the streaming kernels
-    const int tot_c = __shfl(ic, 63), tot_a = __shfl(ia, 63);
+    // read by the streaming kernels, which stream an expert's weights once per
+    // block of 32 positions: the tiled kernels take the call once those
+    // re-reads reach half the active experts' weights, or one expert has more
+    // than 512 pairs
+    const int tot_b = __shfl(ib, 63), tot_a = __shfl(ia, 63);
     const int mode = split == 0 ? 1
                      : split == INT_MAX ? 0
-                     : (tot_c >= split * tot_a || mx > 4 * split) ? 1 : 0;
+                     : (2 * tot_b >= 3 * tot_a || mx > 512) ? 1 : 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int ex = lane * 4 + j;

@@ -13,9 +13,10 @@ struct Plan {
     int bm;             // block_m
     int path;           // 0 streaming (decode), 1 tiled (prefill)
     int split;          // INT_MAX: streaming kernels only; 0: tiled kernels only;
-                        // else chosen per call on the device: tiled if the active
-                        // pairs average >= split per active expert or one expert
-                        // has more than 4 * split (the mode record after meta)
+                        // else (1) chosen per call on the device: tiled if the
+                        // blocks of <= 32 positions number >= 1.5 x the active
+                        // experts or one expert has more than 512 pairs (the
+                        // mode record after meta)
     float thr;          // mask logit threshold: m = [z >= thr]
     // select / compaction
     int s_ts;           // tokens per select tile (64)

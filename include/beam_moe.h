@@ -66,8 +66,9 @@ extern "C" {
                                          Without a flag, where allowed and
                                          T > 512, the device picks per call from
                                          the routed counts: tiled kernels if the
-                                         active pairs average >= 40 per active
-                                         expert or one expert has > 160, else
+                                         blocks of <= 32 positions per expert
+                                         number >= 1.5 x the active experts, or
+                                         one expert has > 512 active pairs, else
                                          the streaming kernels                 */
 
 /* stage ids for the optional per-stage events of beam_moe_forward_ex */

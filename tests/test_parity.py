@@ -119,12 +119,13 @@ def test_prefill_and_decode_paths_agree():
 
 
 # ---- default above 512 tokens: the device picks, per call, the tiled kernels
-# (active pairs average >= 40 per active expert, or one expert above 160) or
-# the streaming kernels; skewed routing at E=16 lands on the tiled side (one
-# expert above 160), at E=32 on the streaming side
+# (blocks of <= 32 positions number >= 1.5 x the active experts, or one expert
+# above 512 pairs) or the streaming kernels; skewed routing at E=16 lands on
+# the tiled side, at E=32 on the streaming side
 def _expects_tiled(counts):
     act = counts[counts > 0]
-    return counts.sum() >= 40 * len(act) or counts.max() > 160
+    blocks = ((act + 31) // 32).sum()
+    return 2 * blocks >= 3 * len(act) or counts.max() > 512
 
 
 @pytest.mark.parametrize("E,tiled", [(16, True), (32, False)])
