@@ -77,6 +77,31 @@ def parse():
 
 
 # ---------------------------------------------------------------------------
+HERE = os.path.dirname(os.path.abspath(__file__))
+COUNTERS = os.path.join(HERE, "profiles", "decode_d2048_E128_K8_I768_T256_hbm_counters.md")
+
+
+def counted_traffic():
+    """Calibrated HBM bytes per launch of the dominant decode kernel, from the
+    committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary of the headline
+    workload; None when that summary is missing or the kernel source has
+    changed since the counters were taken."""
+    import hashlib
+    try:
+        kv = {}
+        for line in open(COUNTERS):
+            line = line.strip()
+            if line.startswith("traffic_") and ":" in line:
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+        src = os.path.join(HERE, kv["traffic_source"])
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv["traffic_source_sha256"]:
+            return None
+        return {"kernel": kv["traffic_kernel"], "bytes": int(kv["traffic_bytes_per_launch"])}
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def algorithmic(n_act, P, T, d, E, I):
     """Algorithmic HBM bytes and FLOPs of one layer call and of its stages.
 
@@ -302,9 +327,14 @@ def main():
     dom = max(km, key=km.get)
     alg = head["_alg"]
     achieved = alg[dom] / (km[dom] * 1e-3) / 1e9
+    # counted bytes apply to the headline workload and the up kernel they were taken on
+    tr = counted_traffic() if (dom == "up" and args.T == 256 and args.mask_bias == -1.04) else None
     roofline = {"bound": "hbm", "kernel": f"expert_{dom}", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": None, "alg_bytes_per_launch": alg[dom],
+                "traffic": tr["bytes"] if tr else None,
+                "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                "copy-calibrated)" if tr else None,
+                "alg_bytes_per_launch": alg[dom],
                 "avg_launch_ms": round(km[dom], 5),
                 "other": {k: {"avg_launch_ms": round(v, 5),
                               "GBps": round(alg[k] / (v * 1e-3) / 1e9, 1)}
