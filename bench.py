@@ -12,12 +12,17 @@ Phi(-1.04) = 0.149, the paper's ~85% FLOP cut).  Steps rotate over several
 independently drawn weight sets (as the layers of a model would) so that the
 256 MB infinity cache cannot serve repeated weights.
 
-Printed on one JSON line: tokens/s (value), ms per step, the HBM roofline of
-the dominant kernel (per-stage HIP events recorded on the launch stream
-inside the timed steps), the whole-layer HBM fraction, the same kernels with
-the mask forced all-ones (W_mask = 0, plain Top-K), a sweep over the decode
-batch sizes, and the fp64 oracle timed on this host's cores on a bounded
-sample of the same workload.
+Printed on one JSON line: tokens/s (value), ms per step, per-call HIP-event
+durations (median, p10, p90), the HBM roofline of the dominant kernel
+(per-stage HIP events recorded on the launch stream inside the timed steps),
+the whole-layer HBM fraction, this GPU's measured copy/read bandwidth and
+bf16 MFMA rate, the same kernels with the mask forced all-ones (W_mask = 0,
+plain Top-K), a sweep over the decode batch sizes, the prefill runs (keep
+0.15 / 0.3 / 0.5 / 1.0 at T = 2048 and 8192, and the skewed T = 16384 load),
+a stack of 48 distinct layers at T = 64 under the skewed load (eager and as
+one replayed HIP graph), the d=4096/I=1536 layer (decode T = 1 and 64,
+prefill T = 4096, keep 0.15 and 0.5), and the fp64 oracle timed on this
+host's cores on a bounded sample of the headline workload.
 """
 from __future__ import annotations
 
@@ -70,6 +75,16 @@ def parse():
     ap.add_argument("--no-skew", dest="skew", action="store_false")
     ap.add_argument("--only-headline", action="store_true",
                     help="measure the headline workload only (no all-ones run, no sweep)")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured copy/read/MFMA peaks")
+    ap.add_argument("--stack", action="store_true", default=True,
+                    help="also time the 48-layer stack at T=64 under the skewed load")
+    ap.add_argument("--no-stack", dest="stack", action="store_false")
+    ap.add_argument("--stack-T", type=int, default=64)
+    ap.add_argument("--stack-steps", type=int, default=20)
+    ap.add_argument("--large", action="store_true", default=True,
+                    help="also measure the d=4096/I=1536 layer (decode T=1, 64; prefill 4096)")
+    ap.add_argument("--no-large", dest="large", action="store_false")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (torch) three times, so that "
                          "hardware byte counters can be scaled by a copy of known size")
@@ -117,6 +132,22 @@ def algorithmic(n_act, P, T, d, E, I):
     return {"up": up, "down": down, "layer": layer, "flops": flops}
 
 
+def pct(vals, q):
+    """The q-quantile (0..1) of vals, linear between order statistics."""
+    v = sorted(vals)
+    if not v:
+        return None
+    x = q * (len(v) - 1)
+    i = int(math.floor(x))
+    j = min(i + 1, len(v) - 1)
+    return v[i] + (v[j] - v[i]) * (x - i)
+
+
+def dist(vals):
+    return {"median_ms": round(pct(vals, 0.5), 5), "p10_ms": round(pct(vals, 0.1), 5),
+            "p90_ms": round(pct(vals, 0.9), 5), "n": len(vals)}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -125,7 +156,6 @@ def main():
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import dynamic_expert_sparsity_amd as B
@@ -138,18 +168,28 @@ def main():
     torch.cuda.set_device(dev)
     B.lib()
 
+    peaks = None
+    if not args.no_peaks:
+        from dynamic_expert_sparsity_amd import peak
+        peaks = peak.measure(dev)
+        log(f"measured peaks: copy {peaks['copy_GBps']} GB/s, read {peaks['read_GBps']} GB/s, "
+            f"MFMA bf16 {peaks['mfma_bf16_TFLOPs']} TFLOP/s")
+
     shape = synth.SHAPES["qwen3"]
     d, E, K, I = shape.d, shape.E, shape.K, shape.I
     sweep = [int(v) for v in args.sweep.split(",") if v.strip()] if args.sweep else []
+    if args.only_headline:
+        sweep = []
     T_max = max([args.T] + sweep)
 
     # weight sets: enough that the bytes touched between two uses of one set
-    # exceed the 256 MB infinity cache by a wide margin
+    # exceed the 256 MB infinity cache by a wide margin (48 also gives the
+    # 48-layer stack distinct weights per layer)
     per_set_bytes = E * 3 * d * I * 2
     if args.sets:
         n_sets = args.sets
     else:
-        n_sets = 4 if not sweep else 48
+        n_sets = 4 if args.only_headline else 48
     free, total = torch.cuda.mem_get_info()
     n_sets = max(1, min(n_sets, int(0.6 * free // per_set_bytes)))
     log(f"drawing {n_sets} weight sets ({n_sets * per_set_bytes / 1e9:.1f} GB) on {dev}")
@@ -160,12 +200,9 @@ def main():
     torch.cuda.synchronize()
     log(f"drawn in {time.time() - t0:.1f}s")
 
-    stream = torch.cuda.current_stream()
-
-    def make_layers(T, allones=False, ns=n_sets):
+    def make_layers(T, allones=False):
         Ls = []
-        for s in range(ns):
-            S = sets[s]
+        for S in sets:
             Ls.append((B.MoELayer(S["W_gate"], zeros_mask if allones else S["W_mask"], S["W_gu"],
                                   S["W_dt"], K), S["x"][:T].contiguous()))
         return Ls
@@ -175,9 +212,11 @@ def main():
 
         events=None: no events (the clean timing).  events="stages": one event
         between every two stages (diagnostic: each record adds a few us).
-        events=<stage name>: two events bracketing that stage only, on the
-        launch stream, averaged over the steps (the kernel's launch duration).
-        Returns (ms per step, dict of per-stage ms per step or None)."""
+        events="call": two events bracketing each whole call (per-call
+        durations).  events=<stage name>: two events bracketing that stage
+        only, on the launch stream (the kernel's launch duration).
+        Returns (ms per step, dict of per-stage ms per step or None, list of
+        per-step ms of the bracketed span or None)."""
         ns = len(Ls)
         for lay, x in Ls:  # buffers of every layer allocated before any timing
             lay.prepare(x.shape[0])
@@ -187,7 +226,9 @@ def main():
         n_ev = len(B.STAGES) + 1
         ev = B.HipEvents(n_ev * steps) if events else None
         slots = None
-        if events and events != "stages":
+        if events == "call":
+            slots = (0, n_ev - 1)
+        elif events and events != "stages":
             j = B.STAGES.index(events)
             slots = (j, j + 1)
         torch.cuda.synchronize()
@@ -203,12 +244,13 @@ def main():
                 lay(x, events=hs)
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) * 1e3 / steps
-        stages = None
+        stages, per = None, None
         if ev is not None:
             stages = {}
             if slots:
-                stages[events] = sum(ev.elapsed_ms(i * n_ev + slots[0], i * n_ev + slots[1])
-                                     for i in range(steps)) / steps
+                per = [ev.elapsed_ms(i * n_ev + slots[0], i * n_ev + slots[1])
+                       for i in range(steps)]
+                stages[events] = sum(per) / steps
             else:
                 for j, name in enumerate(B.STAGES):
                     stages[name] = sum(ev.elapsed_ms(i * n_ev + j, i * n_ev + j + 1)
@@ -216,10 +258,10 @@ def main():
                 stages["gpu_total"] = sum(ev.elapsed_ms(i * n_ev, i * n_ev + n_ev - 1)
                                           for i in range(steps)) / steps
             ev.close()
-        return ms, stages
+        return ms, stages, per
 
     def counts(Ls):
-        """Active pairs and active experts per set (from the last call's routing)."""
+        """Active pairs and active experts per entry (from one call each)."""
         out = []
         for lay, x in Ls:
             lay(x)
@@ -228,24 +270,24 @@ def main():
             out.append((na[0], na[2]))
         return out
 
-    def measure(T, steps, warmup, allones=False, kernels=()):
-        ns = n_sets
-        Ls = make_layers(T, allones, ns)
-        ms, _ = timed(Ls, steps, warmup)
-        _, stages = timed(Ls, max(20, steps // 4), 5, events="stages")
+    def measure(Ls, T, steps, warmup, dims=(d, E, K, I), kernels=()):
+        d_, E_, K_, I_ = dims
+        ms, _, _ = timed(Ls, steps, warmup)
+        _, _, per = timed(Ls, steps, 5, events="call")
+        _, stages, _ = timed(Ls, max(20, steps // 4), 5, events="stages")
         kern = {k: timed(Ls, steps, 5, events=k)[1][k] for k in kernels}
         cs = counts(Ls)
         P = sum(c[0] for c in cs) / len(cs)
         n_act = sum(c[1] for c in cs) / len(cs)
-        alg = algorithmic(n_act, P, T, d, E, I)
+        alg = algorithmic(n_act, P, T, d_, E_, I_)
         r = {"T": T, "ms_per_step": ms, "tok_per_s": T / (ms * 1e-3),
-             "active_pairs": P, "active_experts": n_act, "keep_rate": P / (T * K),
+             "per_call": dist(per),
+             "active_pairs": P, "active_experts": n_act, "keep_rate": P / (T * K_),
              "layer_bytes": alg["layer"], "layer_GBps": alg["layer"] / (ms * 1e-3) / 1e9}
         r["layer_hbm_frac"] = r["layer_GBps"] / HBM_PEAK_GBPS
         r["stages_ms_evented"] = stages
         r["kernel_ms"] = kern
         r["_alg"] = alg
-        del Ls
         return r
 
     if args.calibrate_copy:
@@ -258,6 +300,32 @@ def main():
         del src, dst
 
     # ---- prefill: tiled grouped-GEMM path, MFMA utilisation ---------------
+    def prefill_entry(Ls, T, b, skew, steps, dims=(d, E, K, I)):
+        d_, E_, K_, I_ = dims
+        ms, _, _ = timed(Ls, steps, 3)
+        _, _, per = timed(Ls, steps, 2, events="call")
+        kern = {k: timed(Ls, steps, 2, events=k)[1][k] for k in ("router", "up", "down")}
+        cs = counts(Ls)
+        P = sum(c[0] for c in cs) / len(cs)
+        n_act = sum(c[1] for c in cs) / len(cs)
+        alg = algorithmic(n_act, P, T, d_, E_, I_)
+        fl_up = 4.0 * d_ * I_ * P
+        fl_dn = 2.0 * d_ * I_ * P
+        out = {"T": T, "mask_bias": None if skew else b, "skew": skew,
+               "keep_rate": round(P / (T * K_), 4), "active_pairs": P,
+               "ms_per_step": round(ms, 5), "tok_per_s": round(T / (ms * 1e-3), 1),
+               "per_call": dist(per),
+               "mfma_frac_layer": round(alg["flops"] / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+               "hbm_frac_layer": round(alg["layer"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+               "kernel_ms": {k: round(v, 5) for k, v in kern.items()},
+               "mfma_frac_up": round(fl_up / (kern["up"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+               "mfma_frac_down": round(fl_dn / (kern["down"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+               # the larger of the two floors: weight bytes at peak HBM, FLOPs at peak MFMA
+               "roofline_ms": round(max(alg["layer"] / (HBM_PEAK_GBPS * 1e9),
+                                        alg["flops"] / (BF16_PEAK_TFLOPS * 1e12)) * 1e3, 5)}
+        out["roofline_frac"] = round(out["roofline_ms"] / ms, 4)
+        return out
+
     def measure_prefill(T, b, skew=False, steps=args.prefill_steps):
         n = min(2, n_sets)
         Ls = []
@@ -271,26 +339,7 @@ def main():
                 x = synth.make_tokens(shape, T, seed=0, layer=s, device=dev)
                 Ls.append((B.MoELayer(S["W_gate"], synth.with_mask_bias(S["W_mask"], b),
                                       S["W_gu"], S["W_dt"], K, flags=args.prefill_flags), x))
-        ms, _ = timed(Ls, steps, 3)
-        kern = {k: timed(Ls, steps, 2, events=k)[1][k] for k in ("router", "up", "down")}
-        cs = counts(Ls)
-        P = sum(c[0] for c in cs) / len(cs)
-        n_act = sum(c[1] for c in cs) / len(cs)
-        alg = algorithmic(n_act, P, T, d, E, I)
-        fl_up = 4.0 * d * I * P
-        fl_dn = 2.0 * d * I * P
-        out = {"T": T, "mask_bias": None if skew else b, "skew": skew,
-               "keep_rate": round(P / (T * K), 4), "active_pairs": P,
-               "ms_per_step": round(ms, 5), "tok_per_s": round(T / (ms * 1e-3), 1),
-               "mfma_frac_layer": round(alg["flops"] / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-               "hbm_frac_layer": round(alg["layer"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-               "kernel_ms": {k: round(v, 5) for k, v in kern.items()},
-               "mfma_frac_up": round(fl_up / (kern["up"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-               "mfma_frac_down": round(fl_dn / (kern["down"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-               # the larger of the two floors: weight bytes at peak HBM, FLOPs at peak MFMA
-               "roofline_ms": round(max(alg["layer"] / (HBM_PEAK_GBPS * 1e9),
-                                        alg["flops"] / (BF16_PEAK_TFLOPS * 1e12)) * 1e3, 5)}
-        out["roofline_frac"] = round(out["roofline_ms"] / ms, 4)
+        out = prefill_entry(Ls, T, b, skew, steps)
         del Ls
         return out
 
@@ -317,12 +366,14 @@ def main():
 
     # ---- headline --------------------------------------------------------
     log(f"headline: T={args.T}, {args.steps} steps after {args.warmup} warm-up")
-    head = measure(args.T, args.steps, args.warmup, kernels=("up", "down"))
+    Ls = make_layers(args.T)
+    head = measure(Ls, args.T, args.steps, args.warmup, kernels=("up", "down"))
+    del Ls
     ones = None
     if not args.only_headline:
-        ones = measure(args.T, args.steps, args.warmup, allones=True, kernels=("up", "down"))
-    else:
-        sweep = []
+        Ls = make_layers(args.T, allones=True)
+        ones = measure(Ls, args.T, args.steps, args.warmup, kernels=("up", "down"))
+        del Ls
     km = head["kernel_ms"]
     dom = max(km, key=km.get)
     alg = head["_alg"]
@@ -336,6 +387,8 @@ def main():
                                 "copy-calibrated)" if tr else None,
                 "alg_bytes_per_launch": alg[dom],
                 "avg_launch_ms": round(km[dom], 5),
+                "measured_peak": peaks["read_GBps"] if peaks else None,
+                "frac_of_measured_peak": round(achieved / peaks["read_GBps"], 4) if peaks else None,
                 "other": {k: {"avg_launch_ms": round(v, 5),
                               "GBps": round(alg[k] / (v * 1e-3) / 1e9, 1)}
                           for k, v in km.items() if k != dom}}
@@ -343,8 +396,11 @@ def main():
     # ---- sweep -------------------------------------------------------------
     sweep_out = []
     for T in sweep:
-        m = measure(T, args.sweep_steps, 10)
-        o = measure(T, args.sweep_steps, 10, allones=True)
+        Ls = make_layers(T)
+        m = measure(Ls, T, args.sweep_steps, 10)
+        Ls = make_layers(T, allones=True)
+        o = measure(Ls, T, args.sweep_steps, 10)
+        del Ls
         sweep_out.append({
             "T": T,
             "masked": {k: _r(v) for k, v in m.items() if not k.startswith("_")},
@@ -355,12 +411,28 @@ def main():
         log(f"sweep T={T}: masked {m['ms_per_step']*1e3:.1f} us, "
             f"all-ones {o['ms_per_step']*1e3:.1f} us")
 
+    # ---- 48-layer stack at T = 64, skewed load ------------------------------
+    stack = None
+    if args.stack and not args.only_headline:
+        stack = run_stack(B, synth, sets, shape, dev, args.stack_T, args.stack_steps,
+                          dims=(d, E, K, I))
+        log(f"stack: {stack['layers']} layers at T={stack['T']}: eager "
+            f"{stack['eager']['ms_per_step']:.3f} ms, graph {stack['graph']['ms_per_step']:.3f} ms "
+            f"per step")
+
     prefill_out = [] if args.only_headline else run_prefill()
 
     # ---- CPU baseline: the fp64 oracle on this host's cores ---------------
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(sets, args.T, K, args.cpu_seconds)
+
+    # ---- the larger layer: d=4096, I=1536 -----------------------------------
+    large = None
+    if args.large and not args.only_headline:
+        del sets
+        torch.cuda.empty_cache()
+        large = run_large(B, synth, dev, measure, prefill_entry, args)
 
     out = {
         "metric": METRIC,
@@ -381,21 +453,142 @@ def main():
                    "keep_rate": round(head["keep_rate"], 4),
                    "active_experts": head["active_experts"], "parallelism": "none (1 GPU)"},
         "roofline": roofline,
+        "per_call": head["per_call"],
         "layer_hbm": {"bytes": head["layer_bytes"], "GBps": round(head["layer_GBps"], 1),
                       "frac": round(head["layer_hbm_frac"], 4)},
+        "measured_peaks": peaks,
         "stages_ms_evented": _r(head["stages_ms_evented"]),
         "allones": None if ones is None else {
             "ms_per_step": round(ones["ms_per_step"], 5),
             "tok_per_s": round(ones["tok_per_s"], 1),
+            "per_call": ones["per_call"],
             "active_experts": ones["active_experts"],
             "layer_bytes": ones["layer_bytes"],
             "kernel_ms": _r(ones["kernel_ms"]),
             "speedup_masked_vs_allones": round(ones["ms_per_step"] / head["ms_per_step"], 3)},
         "sweep": sweep_out,
         "prefill": prefill_out,
+        "stack": stack,
+        "large": large,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def run_stack(B, synth, sets, shape, dev, T, steps, dims):
+    """A stack of distinct layers called back to back on one stream, T tokens
+    each, under the skewed load (Zipf expert popularity, per-token mask bias):
+    eagerly, then as one captured HIP graph replayed per step."""
+    import torch
+
+    d, E, K, I = dims
+    Ls = []
+    for l, S in enumerate(sets):
+        R = synth.make_router(shape, T, seed=4, layer=200 + l, skew=True, device=dev)
+        Ls.append((B.MoELayer(R["W_gate"], R["W_mask"], S["W_gu"], S["W_dt"], K), R["x"]))
+    for lay, x in Ls:
+        lay.prepare(T)
+
+    def step():
+        for lay, x in Ls:
+            lay(x)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    # routing statistics and eager outputs of one step
+    pairs, acts, ys = [], [], []
+    for lay, x in Ls:
+        y, R = lay(x)
+        torch.cuda.synchronize()
+        na = R["num_active"].cpu().tolist()
+        pairs.append(na[0])
+        acts.append(na[2])
+        ys.append(y.clone())
+    byts = sum(algorithmic(a, p, T, d, E, I)["layer"] for a, p in zip(acts, pairs))
+
+    def time_steps(run):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for a, b in evs:
+            a.record()
+            run()
+            b.record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / steps
+        per = [a.elapsed_time(b) for a, b in evs]
+        return {"ms_per_step": round(wall, 5), "tok_per_s": round(T / (wall * 1e-3), 1),
+                "per_step": dist(per), "ms_per_layer": round(wall / len(Ls), 5),
+                "layer_hbm_frac": round(byts / (wall * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+    eager = time_steps(step)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # one eager pass on the capture stream first
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    g.replay()
+    torch.cuda.synchronize()
+    same = all(torch.equal(lay.y, y0) for (lay, _), y0 in zip(Ls, ys))
+    graph = time_steps(g.replay)
+    graph["replay_equals_eager"] = same
+    n = len(Ls)
+    out = {"workload": f"{n} layers d{d}-E{E}-K{K}-I{I}-bf16-T{T}-skew", "layers": n, "T": T,
+           "keep_rate": round(sum(pairs) / (n * T * K), 4),
+           "active_experts_per_layer": round(sum(acts) / n, 2),
+           "bytes_per_step": byts, "eager": eager, "graph": graph}
+    del g, Ls
+    return out
+
+
+def run_large(B, synth, dev, measure, prefill_entry, args):
+    """The d=4096, E=128, K=8, I=1536 layer: decode T = 1 and 64, prefill
+    T = 4096, each at mask biases -1.04 and 0 (keep 0.15 and 0.5)."""
+    import torch
+
+    shp = synth.SHAPES["large"]
+    d, E, K, I = shp.d, shp.E, shp.K, shp.I
+    per_set = E * 3 * d * I * 2
+    free, _ = torch.cuda.mem_get_info()
+    n = max(1, min(4, int(0.5 * free // per_set)))
+    log(f"large layer: drawing {n} weight sets ({n * per_set / 1e9:.1f} GB)")
+    sets = [synth.make_layer(shp, 64, seed=0, layer=300 + s, mask_bias=0.0, device=dev)
+            for s in range(n)]
+    out = []
+    for b in (-1.04, 0.0):
+        masks = [synth.with_mask_bias(S["W_mask"], b) for S in sets]
+        lays = [B.MoELayer(S["W_gate"], m, S["W_gu"], S["W_dt"], K) for S, m in zip(sets, masks)]
+        for T in (1, 64):
+            if T == 1:
+                # distinct single tokens, so repeated calls do not find their
+                # experts in the infinity cache
+                Ls = [(lays[j % n], sets[j % n]["x"][j // n:j // n + 1].contiguous())
+                      for j in range(64)]
+            else:
+                Ls = [(lays[s], sets[s]["x"]) for s in range(n)]
+            m = measure(Ls, T, args.sweep_steps, 10, dims=(d, E, K, I))
+            out.append({"phase": "decode", "mask_bias": b,
+                        **{k: _r(v) for k, v in m.items() if not k.startswith("_")}})
+            log(f"large decode T={T} b={b:+g}: {m['ms_per_step']*1e3:.1f} us, "
+                f"HBM {m['layer_hbm_frac']:.3f}")
+        xs = [synth.make_tokens(shp, 4096, seed=0, layer=300 + s, device=dev)
+              for s in range(min(n, 2))]
+        pl = [B.MoELayer(S["W_gate"], m, S["W_gu"], S["W_dt"], K)
+              for S, m in zip(sets[:len(xs)], masks)]
+        r = prefill_entry(list(zip(pl, xs)), 4096, b, False, args.prefill_steps,
+                          dims=(d, E, K, I))
+        out.append({"phase": "prefill", **r})
+        log(f"large prefill T=4096 b={b:+g}: {r['ms_per_step']*1e3:.1f} us, "
+            f"MFMA {r['mfma_frac_layer']:.3f}, roofline {r['roofline_frac']:.3f}")
+        del lays, pl, xs, masks
+    del sets
+    return {"workload": f"d{d}-E{E}-K{K}-I{I}-bf16", "weight_sets": n, "runs": out}
 
 
 def _r(v):

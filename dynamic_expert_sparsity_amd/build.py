@@ -2,9 +2,10 @@
 
     python -m dynamic_expert_sparsity_amd.build
 
-Compiles every csrc/*.hip translation unit to an object under _build/ (in
-parallel), links them into dynamic_expert_sparsity_amd/libbeam_moe.so and
-replaces the previous library atomically.
+Compiles the layer's csrc/*.hip translation units to objects under _build/
+(in parallel), links them into dynamic_expert_sparsity_amd/libbeam_moe.so and
+replaces the previous library atomically; the measurement kernels
+(csrc/peak.hip) become libbeam_peak.so the same way.
 """
 from __future__ import annotations
 
@@ -20,6 +21,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbeam_moe.so")
 SOURCES = ["router.hip", "compact.hip", "experts.hip", "gemm.hip", "api.hip"]
+PEAK_LIB = os.path.join(PKG, "libbeam_peak.so")
+PEAK_SOURCES = ["peak.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 CFLAGS = [
@@ -43,18 +46,21 @@ def _run(cmd):
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
-    objs = [os.path.join(BUILD, s.replace(".hip", ".o")) for s in srcs]
-    cmds = [[HIPCC, *CFLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(srcs, objs)]
+    libs = [(LIB, SOURCES), (PEAK_LIB, PEAK_SOURCES)]
+    units = [s for _, srcs in libs for s in srcs]
+    objs = {s: os.path.join(BUILD, s.replace(".hip", ".o")) for s in units}
+    cmds = [[HIPCC, *CFLAGS, "-c", os.path.join(CSRC, s), "-o", objs[s]] for s in units]
     with cf.ThreadPoolExecutor(max_workers=min(len(cmds), 8)) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():
                 print(out)
-    tmp = LIB + ".tmp"
-    out = _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
-    if verbose and out.strip():
-        print(out)
-    os.replace(tmp, LIB)
+    for lib, srcs in libs:
+        tmp = lib + ".tmp"
+        out = _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp,
+                    *[objs[s] for s in srcs]])
+        if verbose and out.strip():
+            print(out)
+        os.replace(tmp, lib)
     return LIB
 
 

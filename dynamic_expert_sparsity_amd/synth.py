@@ -39,7 +39,7 @@ from dataclasses import dataclass
 
 import torch
 
-__all__ = ["LayerShape", "SHAPES", "make_layer", "make_tokens", "with_mask_bias",
+__all__ = ["LayerShape", "SHAPES", "make_layer", "make_router", "make_tokens", "with_mask_bias",
            "workload_name"]
 
 
@@ -79,16 +79,14 @@ def _randn(shape, std, dtype, device, gen) -> torch.Tensor:
     return t.to(dtype)
 
 
-def make_layer(shape: LayerShape | str, T: int, *, seed: int = 0, layer: int = 0,
-               mask_bias: float = 0.0, mask_mode: str = "bias", skew: bool = False,
-               n_shared: int = 0, device="cpu") -> dict:
-    """Return dict(x, W_gate, W_mask, W_gu, W_dt[, Ws_gu, Ws_dt]) of torch tensors.
-
-    mask_mode: "bias" (column 0 of W_mask = mask_bias) or "zero" (W_mask = 0).
-    """
+def make_router(shape: LayerShape | str, T: int, *, seed: int = 0, layer: int = 0,
+                mask_bias: float = 0.0, mask_mode: str = "bias", skew: bool = False,
+                device="cpu") -> dict:
+    """Return dict(x, W_gate, W_mask): make_layer's tokens and routers alone
+    (the same values make_layer gives for the same arguments)."""
     if isinstance(shape, str):
         shape = SHAPES[shape]
-    d, E, I, dt = shape.d, shape.E, shape.I, shape.dtype
+    d, E, dt = shape.d, shape.E, shape.dtype
     dev = torch.device(device)
 
     x = _randn((T, d), 1.0, torch.float32, dev, _gen(dev, seed, layer, _TID["x"]))
@@ -125,6 +123,22 @@ def make_layer(shape: LayerShape | str, T: int, *, seed: int = 0, layer: int = 0
         bt[perm[n_pos:n_pos + n_fun]] = -2.0
         if T > 0:
             x[:, 1] = bt.to(dev)
+    return {"x": x.to(dt), "W_gate": W_gate.to(dt), "W_mask": W_mask.to(dt)}
+
+
+def make_layer(shape: LayerShape | str, T: int, *, seed: int = 0, layer: int = 0,
+               mask_bias: float = 0.0, mask_mode: str = "bias", skew: bool = False,
+               n_shared: int = 0, device="cpu") -> dict:
+    """Return dict(x, W_gate, W_mask, W_gu, W_dt[, Ws_gu, Ws_dt]) of torch tensors.
+
+    mask_mode: "bias" (column 0 of W_mask = mask_bias) or "zero" (W_mask = 0).
+    """
+    if isinstance(shape, str):
+        shape = SHAPES[shape]
+    d, E, I, dt = shape.d, shape.E, shape.I, shape.dtype
+    dev = torch.device(device)
+    out = make_router(shape, T, seed=seed, layer=layer, mask_bias=mask_bias,
+                      mask_mode=mask_mode, skew=skew, device=dev)
 
     W_gu = torch.empty((E, 2 * I, d), dtype=dt, device=dev)
     W_dt = torch.empty((E, d, I), dtype=dt, device=dev)
@@ -133,13 +147,8 @@ def make_layer(shape: LayerShape | str, T: int, *, seed: int = 0, layer: int = 0
                          _gen(dev, seed, layer, _TID["W_gu"], e))
         W_dt[e] = _randn((d, I), 1.0 / math.sqrt(I), dt, dev,
                          _gen(dev, seed, layer, _TID["W_dt"], e))
-    out = {
-        "x": x.to(dt),
-        "W_gate": W_gate.to(dt),
-        "W_mask": W_mask.to(dt),
-        "W_gu": W_gu,
-        "W_dt": W_dt,
-    }
+    out["W_gu"] = W_gu
+    out["W_dt"] = W_dt
     if n_shared > 0:
         Ws_gu = torch.empty((n_shared, 2 * I, d), dtype=dt, device=dev)
         Ws_dt = torch.empty((n_shared, d, I), dtype=dt, device=dev)
