@@ -19,6 +19,7 @@ __all__ = [
     "BEAM_F32", "BEAM_BF16", "BEAM_FORCE_DECODE", "BEAM_FORCE_PREFILL",
     "STAGES", "BeamError", "lib", "library_path", "Desc", "Routing", "Sizes",
     "make_desc", "query", "alloc_routing", "route", "forward", "MoELayer", "HipEvents",
+    "RoutingStats",
 ]
 
 BEAM_OK, BEAM_EINVAL, BEAM_EUNSUPPORTED, BEAM_EWORKSPACE, BEAM_EHIP = 0, -1, -2, -3, -4
@@ -86,6 +87,9 @@ def lib() -> ctypes.CDLL:
         L.beam_moe_forward_ex.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, vp, vp, vp,
                                           ctypes.POINTER(Routing), vp, sz, vp, vp]
         L.beam_moe_forward_ex.restype = ctypes.c_int
+        L.beam_moe_stats.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Routing), vp, vp, vp,
+                                     vp]
+        L.beam_moe_stats.restype = ctypes.c_int
         L.beam_moe_strerror.argtypes = [ctypes.c_int]
         L.beam_moe_strerror.restype = ctypes.c_char_p
         L.beam_moe_last_error.argtypes = []
@@ -265,6 +269,36 @@ class MoELayer:
         return self.y, self.routing
 
     __call__ = forward
+
+    def stats(self, counters: "RoutingStats", stream=None):
+        """Add the statistics of this layer's last routing to `counters`."""
+        counters.add(self.desc, self.routing, stream)
+
+
+class RoutingStats:
+    """64-bit device counters filled by beam_moe_stats, summed over calls:
+    rank_masked [K], active_hist [K+1], expert_load [E] (int64 tensors)."""
+
+    def __init__(self, E, K, device):
+        z = lambda n: torch.zeros(n, dtype=torch.int64, device=device)  # noqa: E731
+        self.rank_masked, self.active_hist, self.expert_load = z(K), z(K + 1), z(E)
+        self.E, self.K = E, K
+
+    def add(self, desc: Desc, R: dict, stream=None):
+        """Add the statistics of routing R (described by desc) on the stream."""
+        if desc.E != self.E or desc.K != self.K:
+            raise ValueError("counters were made for another E or K")
+        for name in ("mask", "masked_ids"):
+            _gpu_tensor(name, R[name], shape=(desc.T, desc.K))
+        rs = Routing(**{n: 0 for n in _ROUTING_FIELDS})
+        rs.mask, rs.masked_ids = R["mask"].data_ptr(), R["masked_ids"].data_ptr()
+        _check(lib().beam_moe_stats(ctypes.byref(desc), ctypes.byref(rs),
+                                    self.rank_masked.data_ptr(), self.active_hist.data_ptr(),
+                                    self.expert_load.data_ptr(), _stream_ptr(stream)))
+
+    def zero_(self):
+        for t in (self.rank_masked, self.active_hist, self.expert_load):
+            t.zero_()
 
 
 def route(x, W_gate, W_mask, K, block_m=0, flags=0, tau=0.0, stream=None) -> dict:

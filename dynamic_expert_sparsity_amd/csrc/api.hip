@@ -246,6 +246,29 @@ int beam_moe_forward(const beam_moe_desc *desc, const void *x, const void *W_gat
                                nullptr);
 }
 
+int beam_moe_stats(const beam_moe_desc *desc, const beam_moe_routing *routing,
+                   uint64_t *rank_masked, uint64_t *active_hist, uint64_t *expert_load,
+                   hipStream_t stream) {
+    Plan p;
+    int rc = make_plan(desc, p);
+    if (rc) return rc;
+    if (!routing) return fail(BEAM_EINVAL, "routing struct is NULL");
+    if (!routing->mask) return fail(BEAM_EINVAL, "routing.mask is NULL");
+    if (!aligned(routing->masked_ids, 4))
+        return fail(BEAM_EINVAL, "routing.masked_ids is NULL or not 4-byte aligned");
+    const void *outs[] = {rank_masked, active_hist, expert_load};
+    const char *names[] = {"rank_masked", "active_hist", "expert_load"};
+    for (int i = 0; i < 3; ++i)
+        if (outs[i] && !aligned(outs[i], 8))
+            return fail(BEAM_EINVAL, "%s is not 8-byte aligned", names[i]);
+    if (p.T == 0 || (!rank_masked && !active_hist && !expert_load)) return BEAM_OK;
+    Routing r{};
+    r.mask = routing->mask;
+    r.masked_ids = routing->masked_ids;
+    BEAM_TRY(launch_stats(p, r, rank_masked, active_hist, expert_load, stream), "statistics");
+    return BEAM_OK;
+}
+
 const char *beam_moe_strerror(int status) {
     switch (status) {
         case BEAM_OK: return "ok";

@@ -72,5 +72,8 @@ hipError_t launch_expert_down(const Plan &p, const void *W_dt, const Routing &r,
                               const Work &w, hipStream_t s);
 hipError_t launch_combine(const Plan &p, const Routing &r, const Work &w, void *y,
                           hipStream_t s);
+// routing statistics added to caller-owned 64-bit counters (NULL: skipped)
+hipError_t launch_stats(const Plan &p, const Routing &r, uint64_t *rank_masked,
+                        uint64_t *active_hist, uint64_t *expert_load, hipStream_t s);
 
 }  // namespace beam

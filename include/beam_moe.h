@@ -164,6 +164,25 @@ int beam_moe_forward_ex(const beam_moe_desc *desc, const void *x, const void *W_
                         size_t ws_bytes, hipStream_t stream,
                         hipEvent_t *stage_events);
 
+/* beam_moe_stats: routing statistics, accumulated on the device.  They are
+ * the quantities of the paper's analysis of the learned mask (news article on
+ * the paper, section 7: how often the expert of each rank is masked, how many
+ * experts a token activates, how evenly the experts are loaded).
+ * routing: the mask [T, K] and masked_ids [T, K] of a routing of `desc`
+ * (written by beam_moe_route or beam_moe_forward, enqueued earlier on the
+ * same stream); no other field is read.  ADDS, as 64-bit integers, to:
+ *   rank_masked [K]    tokens whose slot k (the k-th largest router logit)
+ *                      is masked; rank_masked[k] / T = mask probability
+ *   active_hist [K+1]  tokens with exactly j active slots, j = 0..K
+ *   expert_load [E]    active pairs of each expert
+ * Each output is a caller-owned, 8-byte aligned device array, or NULL (not
+ * computed).  Zero them before the first call; the sums are exact and do
+ * not depend on the order of the additions.  Returns BEAM_EINVAL for a bad
+ * descriptor, a NULL mask or masked_ids or a misaligned output. */
+int beam_moe_stats(const beam_moe_desc *desc, const beam_moe_routing *routing,
+                   uint64_t *rank_masked, uint64_t *active_hist, uint64_t *expert_load,
+                   hipStream_t stream);
+
 /* Text for a status code (static storage). */
 const char *beam_moe_strerror(int status);
 

@@ -59,6 +59,7 @@ __all__ = [
     "route_from_logits",
     "swiglu_expert",
     "forward",
+    "routing_stats",
 ]
 
 
@@ -225,6 +226,42 @@ def route(x, W_gate, W_mask, K: int, block_m: int = 16, tau: float = 0.5) -> dic
     """Routing from scratch: Eq. 4-7 on fp64 logits, then the grouping."""
     r, z = router_logits(x, W_gate, W_mask)
     return route_from_logits(r, z, K, block_m, tau)
+
+
+# ---------------------------------------------------------------------------
+# Routing statistics (the paper's analyses of the learned mask: how often the
+# slot of each rank is masked, how many experts a token keeps, the load of
+# each expert; news article section 7)
+# ---------------------------------------------------------------------------
+def routing_stats(mask, masked_ids, E: int) -> dict:
+    """Counts over one routing, by plain loops over the tokens.
+
+    mask [T, K] in {0, 1}; slot k holds the expert of the k-th largest router
+    logit (reading R5), so "rank k" is slot k.  Returns int64 arrays:
+      rank_masked[K]   tokens whose rank-k slot is masked
+      active_hist[K+1] tokens with exactly j active slots, j = 0..K
+      expert_load[E]   active pairs of each expert (masked ids -1 excluded,
+                       as in the grouping)
+    The mask probability of rank k is rank_masked[k] / T; the mean number of
+    active experts per token is sum_j j * active_hist[j] / T.
+    """
+    m = np.asarray(mask)
+    mi = np.asarray(masked_ids)
+    T, K = m.shape
+    rank_masked = np.zeros(K, dtype=np.int64)
+    active_hist = np.zeros(K + 1, dtype=np.int64)
+    expert_load = np.zeros(E, dtype=np.int64)
+    for t in range(T):
+        n_active = 0
+        for k in range(K):
+            if m[t, k]:
+                n_active += 1
+                expert_load[int(mi[t, k])] += 1
+            else:
+                rank_masked[k] += 1
+        active_hist[n_active] += 1
+    return {"rank_masked": rank_masked, "active_hist": active_hist,
+            "expert_load": expert_load}
 
 
 # ---------------------------------------------------------------------------

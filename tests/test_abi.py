@@ -123,6 +123,31 @@ def test_short_workspace_rejected():
     assert rc == B.BEAM_EWORKSPACE
 
 
+def test_stats_argument_checks():
+    L = B.lib()
+    d = B.make_desc(4, 256, 16, 2, 64, 1)
+    # NULL routing struct, NULL mask, misaligned counters: EINVAL, nothing enqueued
+    assert L.beam_moe_stats(ctypes.byref(d), None, 0x1000, None, None, None) == B.BEAM_EINVAL
+    r = B.Routing(*[0] * 13)
+    assert L.beam_moe_stats(ctypes.byref(d), ctypes.byref(r), 0x1000, None, None,
+                            None) == B.BEAM_EINVAL
+    assert b"mask" in L.beam_moe_last_error()
+    r.mask, r.masked_ids = 0x2000, 0x3000
+    assert L.beam_moe_stats(ctypes.byref(d), ctypes.byref(r), 0x1004, None, None,
+                            None) == B.BEAM_EINVAL
+    assert b"rank_masked" in L.beam_moe_last_error()
+    # no counter requested, or T = 0: nothing to do
+    assert L.beam_moe_stats(ctypes.byref(d), ctypes.byref(r), None, None, None,
+                            None) == B.BEAM_OK
+    d0 = B.make_desc(0, 256, 16, 2, 64, 1)
+    assert L.beam_moe_stats(ctypes.byref(d0), ctypes.byref(r), 0x1000, 0x1008, 0x1010,
+                            None) == B.BEAM_OK
+    # the descriptor is validated like the layer's
+    bad = B.make_desc(4, 256, 16, 20, 64, 1)
+    assert L.beam_moe_stats(ctypes.byref(bad), ctypes.byref(r), 0x1000, None, None,
+                            None) == B.BEAM_EINVAL
+
+
 def test_zero_tokens_is_a_noop():
     L = B.lib()
     d = B.make_desc(0, 256, 16, 2, 64, 1)

@@ -59,6 +59,10 @@ def test_fig3_worked_example():
     np.testing.assert_allclose(R["g_hat"], [[_expr(s) for s in exp["g_hat_expr"][0]]], rtol=1e-14)
     y = oracle.forward(x, W_gate, W_mask, W_gu, W_dt, K)
     np.testing.assert_allclose(y, [[_expr(s) for s in exp["y_expr"][0]]], rtol=1e-13)
+    S = oracle.routing_stats(R["mask"], R["masked_ids"], W_gate.shape[0])
+    assert S["rank_masked"].tolist() == exp["rank_masked"]
+    assert S["active_hist"].tolist() == exp["active_hist"]
+    assert S["expert_load"].tolist() == exp["expert_load"]
 
 
 # ---------------------------------------------------------------------------
@@ -329,3 +333,81 @@ def test_synth_recipe_shapes_and_bias():
     assert L["W_gu"].shape == (8, 256, 64) and L["W_dt"].shape == (8, 64, 128)
     L2 = synth.make_layer("tiny", 4, seed=0, mask_bias=-1.04)
     assert all(torch.equal(L[k], L2[k]) for k in L)
+
+
+# ---------------------------------------------------------------------------
+# Routing statistics (mask probability by rank, active slots per token,
+# expert load)
+# ---------------------------------------------------------------------------
+def test_stats_rank_is_slot_not_expert():
+    # two tokens with opposite logit orders: token 0 ranks experts 0,1,2,3,
+    # token 1 ranks 3,2,1,0; only expert 0 has z < 0.  Token 0 loses its rank-0
+    # slot, token 1 its rank-3 slot (K = 4), so a count by expert index instead
+    # of by rank would put both at the same index.
+    r = np.array([[4.0, 3.0, 2.0, 1.0], [1.0, 2.0, 3.0, 4.0]])
+    z = np.array([[-1.0, 1.0, 1.0, 1.0], [-1.0, 1.0, 1.0, 1.0]])
+    R = oracle.route_from_logits(r, z, 4, 1)
+    S = oracle.routing_stats(R["mask"], R["masked_ids"], 4)
+    assert S["rank_masked"].tolist() == [1, 0, 0, 1]
+    assert S["active_hist"].tolist() == [0, 0, 0, 2, 0]
+    assert S["expert_load"].tolist() == [0, 2, 2, 2]
+
+
+def test_stats_special_cases():
+    L = _layer_np(synth.make_layer("tiny", 40, seed=11, mask_mode="zero"))
+    K, E = 2, 8
+    R = oracle.route(L["x"], L["W_gate"], L["W_mask"], K)
+    S = oracle.routing_stats(R["mask"], R["masked_ids"], E)
+    assert S["rank_masked"].tolist() == [0, 0]
+    assert S["active_hist"].tolist() == [0, 0, 40]
+    np.testing.assert_array_equal(S["expert_load"],
+                                  np.bincount(R["topk_ids"].ravel(), minlength=E))
+    L = _layer_np(synth.make_layer("tiny", 40, seed=11, mask_bias=-8.0))
+    R = oracle.route(L["x"], L["W_gate"], L["W_mask"], K)
+    S = oracle.routing_stats(R["mask"], R["masked_ids"], E)
+    assert S["rank_masked"].tolist() == [40, 40]
+    assert S["active_hist"].tolist() == [40, 0, 0]
+    assert S["expert_load"].sum() == 0
+
+
+@pytest.mark.parametrize("seed,b", [(12, -0.3), (13, 0.7)])
+def test_stats_invariants(seed, b):
+    L = _layer_np(synth.make_layer("tiny", 300, seed=seed, mask_bias=b))
+    K, E = 2, 8
+    R = oracle.route(L["x"], L["W_gate"], L["W_mask"], K, block_m=4)
+    S = oracle.routing_stats(R["mask"], R["masked_ids"], E)
+    T = 300
+    P = int(np.asarray(R["mask"]).sum())
+    assert S["active_hist"].sum() == T
+    assert (np.arange(K + 1) * S["active_hist"]).sum() == P
+    assert S["rank_masked"].sum() == T * K - P
+    # the load equals the grouping's per-expert counts (a separate routine)
+    np.testing.assert_array_equal(S["expert_load"], R["counts"])
+
+
+def test_stats_binomial_closed_form():
+    # The mask router reads input channels disjoint from the router's and its
+    # rows are orthogonal with equal norm s, so for x_{1..d-1} ~ N(0, 1) the
+    # z_e are independent N(b, s^2) and independent of r: every slot, of any
+    # rank, is kept with probability p = Phi(b / s), independently, and the
+    # number of active slots per token is Binomial(K, p).
+    T, E, K, d = 20000, 8, 4, 64
+    rng = np.random.default_rng(14)
+    x = rng.standard_normal((T, d))
+    x[:, 0] = 1.0
+    W_gate = np.zeros((E, d))
+    W_gate[:, 1:32] = rng.standard_normal((E, 31)) / math.sqrt(31)
+    q, _ = np.linalg.qr(rng.standard_normal((32, E)))   # orthonormal columns
+    s, b = 0.8, -0.4
+    W_mask = np.zeros((E, d))
+    W_mask[:, 32:64] = s * q.T
+    W_mask[:, 0] = b
+    R = oracle.route(x, W_gate, W_mask, K)
+    S = oracle.routing_stats(R["mask"], R["masked_ids"], E)
+    p = _phi(b / s)
+    sd = math.sqrt(p * (1 - p) / T)
+    for k in range(K):
+        assert abs(S["rank_masked"][k] / T - (1 - p)) <= 4 * sd + 1e-3, k
+    for j in range(K + 1):
+        pj = math.comb(K, j) * p ** j * (1 - p) ** (K - j)
+        assert abs(S["active_hist"][j] / T - pj) <= 4 * math.sqrt(pj * (1 - pj) / T) + 1e-3, j
