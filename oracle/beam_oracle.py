@@ -40,6 +40,11 @@ Readings of points the pages leave open (each is also listed in the design doc):
   T1  (threshold variants, the ablation over tau in the news article section
       8) tau != 0.5 is evaluated as z >= ln(tau / (1 - tau)), the exact
       preimage of sigmoid >= tau.
+  S1  (shared experts, news article sections 5 and 6: models with always-on
+      shared experts keep running them for a token whose routed slots are
+      all masked) a shared expert is a SwiGLU expert of the routed experts'
+      shape, applied to every token with weight 1 and no mask, and added to
+      the routed sum of Eq. 8.
 """
 from __future__ import annotations
 
@@ -147,43 +152,52 @@ def aggregate(g, m) -> np.ndarray:
 # Grouping of (token, expert) pairs (news article, section 5: ids of masked
 # experts become -1 and are left out of the per-expert counts)
 # ---------------------------------------------------------------------------
-def compact(masked_ids, E: int, block_m: int) -> dict:
+def compact(masked_ids, E: int, block_m: int, n_shared: int = 0) -> dict:
     """Per-expert counts, block-padded offsets and sorted pair lists.
 
-    masked_ids: [T, K] with -1 for masked slots.  A pair is p = t*K + k.
-    Returns int64 arrays:
-      counts[E]          active pairs routed to each expert (-1 excluded)
-      offsets[E+1]       exclusive prefix sum of counts rounded up to block_m
+    masked_ids: [T, K] with -1 for masked slots.  A routed pair is
+    p = t*K + k.  With n_shared = S always-on shared experts (the pages'
+    DeepSeek and Qwen1.5-MoE models; reading S1), expert E + s also receives
+    every token t as the pair p = T*K + t*S + s.
+    Returns int64 arrays over the E + S experts:
+      counts[E+S]        pairs routed to each expert (-1 excluded)
+      offsets[E+S+1]     exclusive prefix sum of counts rounded up to block_m
       sorted_pairs[num_padded]  per expert, its pair ids ascending, then the
-                         pad value T*K up to the next multiple of block_m
+                         pad value T*(K+S) up to the next multiple of block_m
       block_expert[num_padded // block_m]   expert owning each block
       active_experts[n]  experts with count >= 1, ascending
-      num_active         (P, num_padded)
+      num_active         (P, num_padded), P = all scheduled pairs
     """
     mi = np.asarray(masked_ids)
     T, K = mi.shape
-    pad = T * K
+    S = int(n_shared)
+    E2 = E + S
+    pad = T * (K + S)
     flat = mi.reshape(-1)
-    counts = np.zeros(E, dtype=np.int64)
-    lists = [[] for _ in range(E)]
+    counts = np.zeros(E2, dtype=np.int64)
+    lists = [[] for _ in range(E2)]
     for p in range(T * K):          # ascending pair id -> lists come out sorted
         e = int(flat[p])
         if e < 0:
             continue
         counts[e] += 1
         lists[e].append(p)
-    offsets = np.zeros(E + 1, dtype=np.int64)
-    for e in range(E):
+    for t in range(T):              # shared pairs, ascending in t for each s
+        for s in range(S):
+            counts[E + s] += 1
+            lists[E + s].append(T * K + t * S + s)
+    offsets = np.zeros(E2 + 1, dtype=np.int64)
+    for e in range(E2):
         padded = -(-int(counts[e]) // block_m) * block_m
         offsets[e + 1] = offsets[e] + padded
-    num_padded = int(offsets[E])
+    num_padded = int(offsets[E2])
     sorted_pairs = np.full(num_padded, pad, dtype=np.int64)
     block_expert = np.empty(num_padded // block_m, dtype=np.int64)
-    for e in range(E):
+    for e in range(E2):
         o = int(offsets[e])
         sorted_pairs[o:o + len(lists[e])] = lists[e]
         block_expert[o // block_m:int(offsets[e + 1]) // block_m] = e
-    active = np.array([e for e in range(E) if counts[e] > 0], dtype=np.int64)
+    active = np.array([e for e in range(E2) if counts[e] > 0], dtype=np.int64)
     return {
         "counts": counts,
         "offsets": offsets,
@@ -194,7 +208,8 @@ def compact(masked_ids, E: int, block_m: int) -> dict:
     }
 
 
-def route_from_logits(r, z, K: int, block_m: int = 16, tau: float = 0.5) -> dict:
+def route_from_logits(r, z, K: int, block_m: int = 16, tau: float = 0.5,
+                      n_shared: int = 0) -> dict:
     """Steps 1-4 of section 3.2 plus the grouping, starting from given logits.
 
     Used with the GPU's float32 logits so that every discrete output (ids,
@@ -218,14 +233,15 @@ def route_from_logits(r, z, K: int, block_m: int = 16, tau: float = 0.5) -> dict
         "g_hat": g_hat,
         "masked_ids": masked_ids,
     }
-    out.update(compact(masked_ids, E, block_m))
+    out.update(compact(masked_ids, E, block_m, n_shared))
     return out
 
 
-def route(x, W_gate, W_mask, K: int, block_m: int = 16, tau: float = 0.5) -> dict:
+def route(x, W_gate, W_mask, K: int, block_m: int = 16, tau: float = 0.5,
+          n_shared: int = 0) -> dict:
     """Routing from scratch: Eq. 4-7 on fp64 logits, then the grouping."""
     r, z = router_logits(x, W_gate, W_mask)
-    return route_from_logits(r, z, K, block_m, tau)
+    return route_from_logits(r, z, K, block_m, tau, n_shared)
 
 
 # ---------------------------------------------------------------------------
@@ -286,7 +302,7 @@ def swiglu_expert(xs, Wg, Wu, Wd):
 
 
 def forward(x, W_gate, W_mask, W_gu, W_dt, K: int, routing: dict | None = None,
-            tokens=None, tau: float = 0.5):
+            tokens=None, tau: float = 0.5, shared=None):
     """Masked-MoE layer output y, [T or len(tokens), d] float64 (Eq. 8).
 
     x        [T, d]
@@ -299,9 +315,14 @@ def forward(x, W_gate, W_mask, W_gu, W_dt, K: int, routing: dict | None = None,
              with route() when None.
     tokens   optional subset of token indices; y is returned for those rows
              only (the layer is per token, Eq. 8).
+    shared   optional (Ws_gu, Ws_dt), each indexable by shared expert s like
+             W_gu / W_dt: always-on experts added with weight 1 and never
+             masked (reading S1), so a token whose K slots are all masked
+             still gets their output.
 
     y_t = sum_k g_hat[t,k] * E_{ids[t,k]}(x_t) over the slots with m = 1, in
-    slot order; y_t = 0 when no slot survives (reading R8).  Experts are
+    slot order, after the shared experts' sum (if any); without shared
+    experts y_t = 0 when no slot survives (reading R8).  Experts are
     visited one at a time and only for the tokens routed to them; each
     expert's weights are upcast to float64 when it is visited.
     """
@@ -331,6 +352,12 @@ def forward(x, W_gate, W_mask, W_gu, W_dt, K: int, routing: dict | None = None,
         for j, (i, t, k) in enumerate(items):
             contrib[i, k] = g_hat[t, k] * o[j]
     y = np.zeros((len(rows), d), dtype=np.float64)
+    if shared is not None:
+        Ws_gu, Ws_dt = shared
+        for s in range(len(Ws_gu)):
+            gu = _f64(Ws_gu[s])
+            I = gu.shape[0] // 2
+            y += swiglu_expert(x64[rows], gu[:I], gu[I:], Ws_dt[s])
     for k in range(ids.shape[1]):
         y += contrib[:, k]
     return y

@@ -224,10 +224,40 @@ def test_compact_bruteforce(E, K, bm, data):
     assert C["active_experts"].tolist() == [e for e in range(E) if (flat == e).any()]
 
 
+@settings(max_examples=60, deadline=None)
+@given(st.integers(1, 5), st.integers(1, 3), st.integers(1, 3), st.sampled_from([1, 4, 16]),
+       st.data())
+def test_compact_shared_bruteforce(E, K, S, bm, data):
+    # shared expert E+s receives every token t as pair T*K + t*S + s; the pad
+    # value becomes T*(K+S); routed experts are listed as without them
+    K = min(K, E)
+    T = data.draw(st.integers(0, 6))
+    mi = np.array(data.draw(st.lists(st.lists(st.integers(-1, E - 1), min_size=K, max_size=K),
+                                     min_size=T, max_size=T)), dtype=np.int64).reshape(T, K)
+    C = oracle.compact(mi, E, bm, n_shared=S)
+    C0 = oracle.compact(mi, E, bm)
+    pad = T * (K + S)
+    flat = mi.reshape(-1)
+    pos = 0
+    for e in range(E + S):
+        if e < E:
+            members = [p for p in range(T * K) if flat[p] == e]
+        else:
+            members = [T * K + t * S + (e - E) for t in range(T)]
+        assert C["counts"][e] == len(members)
+        assert C["offsets"][e] == pos
+        assert C["sorted_pairs"][pos:pos + len(members)].tolist() == members
+        padded = math.ceil(len(members) / bm) * bm
+        assert all(v == pad for v in C["sorted_pairs"][pos + len(members):pos + padded])
+        pos += padded
+    np.testing.assert_array_equal(C["counts"][:E], C0["counts"])
+    assert C["num_active"][0] == int((flat >= 0).sum()) + T * S
+
+
 # ---------------------------------------------------------------------------
 # Forward: dense brute force over all N experts (Eq. 2 / Eq. 8 literally)
 # ---------------------------------------------------------------------------
-def _dense_bruteforce(x, Wg, Wm, W_gu, W_dt, K, tau=0.5, use_mask=True):
+def _dense_bruteforce(x, Wg, Wm, W_gu, W_dt, K, tau=0.5, use_mask=True, shared=None):
     """Every expert on every token; routing weights as full N-vectors.
 
     Top-K membership by rank counting; g_i = Softmax(Top-K(r))_i over all N
@@ -253,6 +283,10 @@ def _dense_bruteforce(x, Wg, Wm, W_gu, W_dt, K, tau=0.5, use_mask=True):
             h = torch.nn.functional.silu(a) * u
             Ei = torch.tensor(W_dt[e], dtype=torch.float64) @ h
             y[t] += g[e] * m[e] * Ei
+        for Sgu, Sdt in shared or ():   # always-on experts, weight 1, no mask
+            Sgu = torch.tensor(Sgu, dtype=torch.float64)
+            h = torch.nn.functional.silu(Sgu[:I] @ xt[t]) * (Sgu[I:] @ xt[t])
+            y[t] += torch.tensor(Sdt, dtype=torch.float64) @ h
     return y.numpy()
 
 
@@ -263,6 +297,39 @@ def test_forward_matches_dense_bruteforce(seed, b):
     y = oracle.forward(L["x"], L["W_gate"], L["W_mask"], L["W_gu"], L["W_dt"], 3)
     yd = _dense_bruteforce(L["x"], L["W_gate"], L["W_mask"], L["W_gu"], L["W_dt"], 3)
     np.testing.assert_allclose(y, yd, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("seed,b", [(15, 0.0), (16, -1.04)])
+def test_forward_shared_matches_dense_bruteforce(seed, b):
+    L = _layer_np(synth.make_layer(synth.LayerShape(16, 6, 3, 8, torch.float32), 12,
+                                   seed=seed, mask_bias=b, n_shared=2))
+    sh = (L["Ws_gu"], L["Ws_dt"])
+    y = oracle.forward(L["x"], L["W_gate"], L["W_mask"], L["W_gu"], L["W_dt"], 3, shared=sh)
+    yd = _dense_bruteforce(L["x"], L["W_gate"], L["W_mask"], L["W_gu"], L["W_dt"], 3,
+                           shared=list(zip(*sh)))
+    np.testing.assert_allclose(y, yd, rtol=1e-12, atol=1e-13)
+
+
+def test_shared_experts_serve_fully_masked_tokens():
+    # news article section 5: with shared experts, a token whose routed slots
+    # are all masked is still processed by them; here every slot is masked
+    L = _layer_np(synth.make_layer(synth.LayerShape(16, 6, 3, 8, torch.float32), 10,
+                                   seed=17, mask_bias=-8.0, n_shared=2))
+    sh = (L["Ws_gu"], L["Ws_dt"])
+    y = oracle.forward(L["x"], L["W_gate"], L["W_mask"], L["W_gu"], L["W_dt"], 3, shared=sh)
+    assert np.abs(y).max() > 0
+    # the same experts as routed experts 0 and 1 of a layer with an all-ones
+    # mask router and a gate that always ranks them first get weight 1/2 each
+    # (softmax of two equal logits): y = 2 * that layer's output
+    x = L["x"]
+    Wg = np.zeros((2, 16))
+    Wm = np.zeros((2, 16))
+    y2 = oracle.forward(x, Wg, Wm, L["Ws_gu"], L["Ws_dt"], 2)
+    np.testing.assert_allclose(y, 2 * y2, rtol=1e-13, atol=1e-15)
+    # zero shared weights give the plain layer
+    z = (np.zeros_like(L["Ws_gu"]), np.zeros_like(L["Ws_dt"]))
+    assert np.all(oracle.forward(x, L["W_gate"], L["W_mask"], L["W_gu"], L["W_dt"], 3,
+                                 shared=z) == 0.0)
 
 
 def test_zero_mask_equals_plain_topk_moe():
