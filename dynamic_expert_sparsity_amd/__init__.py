@@ -44,7 +44,8 @@ class Desc(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("K", ctypes.c_int32), ("I", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("block_m", ctypes.c_int32), ("flags", ctypes.c_uint32),
-                ("tau", ctypes.c_float), ("reserved", ctypes.c_int32 * 3)]
+                ("tau", ctypes.c_float), ("n_shared", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 2)]
 
 
 _ROUTING_FIELDS = ["gate_logits", "mask_logits", "topk_ids", "topk_weights", "mask", "g_hat",
@@ -164,10 +165,10 @@ def _dtype_code(dt: torch.dtype) -> int:
     raise TypeError(f"unsupported dtype {dt}; use float32 or bfloat16")
 
 
-def make_desc(T, d, E, K, I, dtype, block_m=0, flags=0, tau=0.0) -> Desc:
+def make_desc(T, d, E, K, I, dtype, block_m=0, flags=0, tau=0.0, n_shared=0) -> Desc:
     code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
     return Desc(int(T), int(d), int(E), int(K), int(I), code, int(block_m), int(flags),
-                float(tau), (ctypes.c_int32 * 3)(0, 0, 0))
+                float(tau), int(n_shared), (ctypes.c_int32 * 2)(0, 0))
 
 
 def query(desc: Desc) -> dict:
@@ -178,11 +179,12 @@ def query(desc: Desc) -> dict:
 
 
 def alloc_routing(desc: Desc, sizes: dict, device) -> dict:
-    T, E, K = desc.T, desc.E, desc.K
+    T, K = desc.T, desc.K
+    E = desc.E + desc.n_shared  # the grouping covers the shared experts too
     f32, i32 = torch.float32, torch.int32
     mk = lambda shape, dt: torch.empty(shape, dtype=dt, device=device)  # noqa: E731
     return {
-        "gate_logits": mk((T, E), f32), "mask_logits": mk((T, E), f32),
+        "gate_logits": mk((T, desc.E), f32), "mask_logits": mk((T, desc.E), f32),
         "topk_ids": mk((T, K), i32), "topk_weights": mk((T, K), f32),
         "mask": mk((T, K), torch.uint8), "g_hat": mk((T, K), f32),
         "masked_ids": mk((T, K), i32), "expert_counts": mk((E,), i32),
@@ -217,18 +219,25 @@ def _stream_ptr(stream) -> int:
 
 class MoELayer:
     """A BEAM masked-MoE layer bound to fixed weights; reuses its output,
-    routing and workspace buffers across calls with the same T."""
+    routing and workspace buffers across calls with the same T.
+
+    W_gu [E+S, 2I, d] and W_dt [E+S, d, I] hold the E routed experts (E from
+    W_gate) followed by S always-on shared experts (S may be 0)."""
 
     def __init__(self, W_gate, W_mask, W_gu, W_dt, K, block_m=0, flags=0, tau=0.0):
         E, d = W_gate.shape
         self.dtype = W_gate.dtype
         _gpu_tensor("W_gate", W_gate, self.dtype, (E, d))
         _gpu_tensor("W_mask", W_mask, self.dtype, (E, d))
+        E2 = W_gu.shape[0]
+        if E2 < E:
+            raise ValueError(f"W_gu has {E2} experts, fewer than the router's {E}")
         I = W_gu.shape[1] // 2
-        _gpu_tensor("W_gu", W_gu, self.dtype, (E, 2 * I, d))
-        _gpu_tensor("W_dt", W_dt, self.dtype, (E, d, I))
+        _gpu_tensor("W_gu", W_gu, self.dtype, (E2, 2 * I, d))
+        _gpu_tensor("W_dt", W_dt, self.dtype, (E2, d, I))
         self.W_gate, self.W_mask, self.W_gu, self.W_dt = W_gate, W_mask, W_gu, W_dt
         self.d, self.E, self.K, self.I = d, E, int(K), I
+        self.S = E2 - E
         self.block_m, self.flags, self.tau = block_m, flags, tau
         self._T = None
 
@@ -242,7 +251,7 @@ class MoELayer:
             return
         dev = self.W_gate.device
         self.desc = make_desc(T, self.d, self.E, self.K, self.I, self.dtype, self.block_m,
-                              self.flags, self.tau)
+                              self.flags, self.tau, self.S)
         self.sizes = query(self.desc)
         self.routing = alloc_routing(self.desc, self.sizes, dev)
         self._rs = _routing_struct(self.routing)
@@ -301,14 +310,15 @@ class RoutingStats:
             t.zero_()
 
 
-def route(x, W_gate, W_mask, K, block_m=0, flags=0, tau=0.0, stream=None) -> dict:
-    """beam_moe_route: routing tensors for x (new buffers)."""
+def route(x, W_gate, W_mask, K, block_m=0, flags=0, tau=0.0, stream=None, n_shared=0) -> dict:
+    """beam_moe_route: routing tensors for x (new buffers); the grouping
+    includes n_shared always-on experts numbered E .. E+n_shared-1."""
     E, d = W_gate.shape
     _gpu_tensor("x", x, W_gate.dtype)
     _gpu_tensor("W_gate", W_gate, x.dtype, (E, d))
     _gpu_tensor("W_mask", W_mask, x.dtype, (E, d))
     T = x.shape[0]
-    desc = make_desc(T, d, E, K, 64, x.dtype, block_m, flags, tau)  # I unused by routing
+    desc = make_desc(T, d, E, K, 64, x.dtype, block_m, flags, tau, n_shared)  # I unused by routing
     sizes = query(desc)
     R = alloc_routing(desc, sizes, x.device)
     ws = torch.empty(max(sizes["route_workspace_bytes"], 256), dtype=torch.uint8, device=x.device)

@@ -51,10 +51,12 @@ int make_plan(const beam_moe_desc *desc, Plan &p) {
         return fail(BEAM_EINVAL, "BEAM_FORCE_DECODE and BEAM_FORCE_PREFILL are exclusive");
     if (!(D.tau == 0.f || (D.tau > 0.f && D.tau < 1.f)))
         return fail(BEAM_EINVAL, "tau must be 0 (meaning 0.5) or lie in (0, 1)");
-    if (D.reserved[0] || D.reserved[1] || D.reserved[2])
+    if (D.n_shared < 0) return fail(BEAM_EINVAL, "n_shared=%d is negative", D.n_shared);
+    if (D.reserved[0] || D.reserved[1])
         return fail(BEAM_EINVAL, "reserved fields must be 0");
 
-    if (D.E > 256) return fail(BEAM_EUNSUPPORTED, "E=%d > 256", D.E);
+    if (D.E + D.n_shared > 256)
+        return fail(BEAM_EUNSUPPORTED, "E + n_shared = %d > 256", D.E + D.n_shared);
     if (D.K > 16) return fail(BEAM_EUNSUPPORTED, "K=%d > 16", D.K);
     if (D.dtype == BEAM_BF16 && (D.d % 128 != 0 || D.I % 64 != 0 || D.I > 2040))
         return fail(BEAM_EUNSUPPORTED,
@@ -66,9 +68,11 @@ int make_plan(const beam_moe_desc *desc, Plan &p) {
         return fail(BEAM_EUNSUPPORTED,
                     "the tiled path needs bf16, d %% 256 == 0, I %% 128 == 0, block_m 0 or 256");
     const long long TK = (long long)D.T * D.K;
-    if (TK > (1ll << 30)) return fail(BEAM_EUNSUPPORTED, "T*K=%lld too large", TK);
+    const long long PT = (long long)D.T * (D.K + D.n_shared);
+    if (PT > (1ll << 30)) return fail(BEAM_EUNSUPPORTED, "T*(K+n_shared)=%lld too large", PT);
 
     p.T = D.T; p.d = D.d; p.E = D.E; p.K = D.K; p.I = D.I;
+    p.S = D.n_shared; p.E2 = D.E + D.n_shared; p.PT = (int)PT;
     p.dtype = D.dtype;
     // decode (weight streaming) for small batches, tiled grouped GEMM above
     p.path = (D.flags & BEAM_FORCE_PREFILL) ||
@@ -87,19 +91,19 @@ int make_plan(const beam_moe_desc *desc, Plan &p) {
     p.s_ts = 64;
     p.n_tiles = (D.T + 63) / 64;
     p.fuse_scatter = p.n_tiles <= 16;
-    p.max_active = (int)(TK < D.E ? TK : D.E);
-    const long long cap_raw = TK + (long long)p.max_active * (p.bm - 1);
+    p.max_active = (int)(PT < p.E2 ? PT : p.E2);
+    const long long cap_raw = PT + (long long)p.max_active * (p.bm - 1);
     p.cap = (cap_raw + p.bm - 1) / p.bm * p.bm;
     p.n_blocks_cap = p.cap / p.bm;
 
     const size_t elt = p.dtype == BEAM_BF16 ? 2 : 4;
     size_t off = 0;
-    p.off_tile_mask = off; off = align_up(off + (size_t)p.n_tiles * D.E * 8, 256);
-    p.off_tile_base = off; off = align_up(off + (size_t)p.n_tiles * D.E * 4, 256);
-    p.off_pair_pos = off;  off = align_up(off + (size_t)TK * 4, 256);
-    p.off_meta = off;      off = align_up(off + (size_t)(D.E + 1) * 16, 256);
+    p.off_tile_mask = off; off = align_up(off + (size_t)p.n_tiles * p.E2 * 8, 256);
+    p.off_tile_base = off; off = align_up(off + (size_t)p.n_tiles * p.E2 * 4, 256);
+    p.off_pair_pos = off;  off = align_up(off + (size_t)PT * 4, 256);
+    p.off_meta = off;      off = align_up(off + (size_t)(p.E2 + 1) * 16, 256);
     // position blocks of <= 32: at most one partial block per active expert
-    p.off_pbt = off;       off = align_up(off + (size_t)(p.max_active + TK / 32 + 1) * 16, 256);
+    p.off_pbt = off;       off = align_up(off + (size_t)(p.max_active + PT / 32 + 1) * 16, 256);
     // sorted tokens, plus 32 slack entries read (not used) past a block end
     p.off_stok = off;      off = align_up(off + (size_t)(p.cap + 32) * 4, 256);
     p.route_bytes = off;

@@ -8,19 +8,19 @@ namespace beam {
 __global__ __launch_bounds__(256) void compact_scatter(Routing r,
                                                       const int32_t *__restrict__ tile_base,
                                                       const uint64_t *__restrict__ tile_mask,
-                                                      int TK, int K, int E,
+                                                      int PT, int TK, int K, int E, int S,
                                                       int32_t *__restrict__ pair_pos,
                                                       int32_t *__restrict__ sorted_tok) {
     const int p = blockIdx.x * 256 + threadIdx.x;
-    if (p >= TK) return;
-    scatter_pair(p, K, E, r, r.expert_offsets, tile_base, tile_mask, pair_pos, sorted_tok);
+    if (p >= PT) return;
+    scatter_pair(p, K, TK, E, S, r, r.expert_offsets, tile_base, tile_mask, pair_pos, sorted_tok);
 }
 
 hipError_t launch_scatter(const Plan &p, const Routing &r, const Work &w, hipStream_t s) {
     if (p.fuse_scatter) return hipSuccess;
-    const int TK = p.T * p.K;
-    compact_scatter<<<(TK + 255) / 256, 256, 0, s>>>(r, w.tile_base, w.tile_mask, TK, p.K, p.E,
-                                                     w.pair_pos, w.sorted_tok);
+    compact_scatter<<<(p.PT + 255) / 256, 256, 0, s>>>(r, w.tile_base, w.tile_mask, p.PT,
+                                                       p.T * p.K, p.K, p.E, p.S, w.pair_pos,
+                                                       w.sorted_tok);
     return hipGetLastError();
 }
 

@@ -107,10 +107,10 @@ __device__ __forceinline__ void offsets_from_counts(const int *s_cnt, int *s_off
 }
 
 // All threads: block -> expert map (one thread per block) and the pad entries
-// of every expert's segment (sorted pair TK, token 0; one wave per expert, its
-// lanes over the pad slots, so the stores coalesce).
+// of every expert's segment (sorted pair `pad`, token 0; one wave per expert,
+// its lanes over the pad slots, so the stores coalesce).
 __device__ __forceinline__ void blocks_and_pads(const int *s_off, const int *s_cnt, int E, int bm,
-                                                int TK, const Routing &r, int32_t *sorted_tok,
+                                                int pad, const Routing &r, int32_t *sorted_tok,
                                                 int tid, int nthreads) {
     const int n_blocks = s_off[E] / bm;
     for (int b = tid; b < n_blocks; b += nthreads) {
@@ -126,46 +126,61 @@ __device__ __forceinline__ void blocks_and_pads(const int *s_off, const int *s_c
     for (int e = tid >> 6; e < E; e += nw) {
         const int end = s_off[e + 1];
         for (int q = s_off[e] + s_cnt[e] + lane; q < end; q += 64) {
-            r.sorted_pairs[q] = TK;
+            r.sorted_pairs[q] = pad;
             sorted_tok[q] = 0;
         }
     }
 }
 
-// Place one pair: its position in its expert's list, and the inverse maps.
-__device__ __forceinline__ void place_pair(int p, int e, int pos, int K, const Routing &r,
+// Place one pair of token t: its position in its expert's list, and the
+// inverse maps.
+__device__ __forceinline__ void place_pair(int p, int t, int pos, const Routing &r,
                                            int32_t *pair_pos, int32_t *sorted_tok) {
     r.sorted_pairs[pos] = p;
-    sorted_tok[pos] = p / K;
+    sorted_tok[pos] = t;
     pair_pos[p] = pos;
 }
 
-__device__ __forceinline__ void scatter_pair(int p, int K, int E, const Routing &r,
+// Pair p < T*K is routed slot (t, k) = (p / K, p % K); p >= T*K is shared
+// expert E + s of token t, p = T*K + t*S + s.  Tile token sets and bases are
+// [tile][E + S].
+__device__ __forceinline__ void scatter_pair(int p, int K, int TK, int E, int S, const Routing &r,
                                              const int *off, const int32_t *tile_base,
                                              const uint64_t *tile_mask, int32_t *pair_pos,
                                              int32_t *sorted_tok) {
-    const int e = r.masked_ids[p];
-    if (e < 0) {
-        pair_pos[p] = -1;
-        return;
+    int e, t;
+    if (p < TK) {
+        e = r.masked_ids[p];
+        if (e < 0) {
+            pair_pos[p] = -1;
+            return;
+        }
+        t = p / K;
+    } else {
+        const int q = p - TK;
+        t = q / S;
+        e = E + (q - t * S);
     }
-    const int t = p / K;
-    const size_t q = (size_t)(t >> 6) * E + e;
-    const int rank = __popcll(tile_mask[q] & ((1ull << (t & 63)) - 1ull));
-    place_pair(p, e, off[e] + tile_base[q] + rank, K, r, pair_pos, sorted_tok);
+    const size_t qi = (size_t)(t >> 6) * (E + S) + e;
+    const int rank = __popcll(tile_mask[qi] & ((1ull << (t & 63)) - 1ull));
+    place_pair(p, t, off[e] + tile_base[qi] + rank, r, pair_pos, sorted_tok);
 }
 
-// Whole-batch compaction by one workgroup of `nthreads` (>= E) threads.
-// Thread (g, e), g = tid / E, sums the popcounts of a contiguous range of
-// tiles for expert e; group partials give every (tile, expert) its base;
-// wave 0 scans the experts into block-padded offsets; then the block map and
-// pads, and (do_scatter) the position of every pair.  LDS: s_part[nthreads],
-// s_cnt[256], s_off[257].
-__device__ __forceinline__ void scan_tiles(const uint64_t *tile_mask, int n_tiles, int E, int bm,
-                                           int K, int TK, const Routing &r, int32_t *tile_base,
-                                           int32_t *pair_pos, int32_t *meta, int32_t *sorted_tok,
-                                           int32_t *pbt, bool do_scatter, int split, int tid,
-                                           int nthreads, int *s_part, int *s_cnt, int *s_off) {
+// Whole-batch compaction by one workgroup of `nthreads` (>= E + S) threads,
+// over the E routed and S shared experts (E2 = E + S; tile token sets
+// [n_tiles][E2]).  Thread (g, e), g = tid / E2, sums the popcounts of a
+// contiguous range of tiles for expert e; group partials give every (tile,
+// expert) its base; wave 0 scans the experts into block-padded offsets; then
+// the block map and pads, and (do_scatter) the position of every pair.  LDS:
+// s_part[nthreads], s_cnt[256], s_off[257].
+__device__ __forceinline__ void scan_tiles(const uint64_t *tile_mask, int n_tiles, int Er, int S,
+                                           int bm, int K, int TK, const Routing &r,
+                                           int32_t *tile_base, int32_t *pair_pos, int32_t *meta,
+                                           int32_t *sorted_tok, int32_t *pbt, bool do_scatter,
+                                           int split, int tid, int nthreads, int *s_part,
+                                           int *s_cnt, int *s_off) {
+    const int E = Er + S;
+    const int PT = TK + (TK / K) * S;
     const int NG = nthreads / E;
     const int g = tid / E;
     const int e = tid - g * E;
@@ -195,10 +210,10 @@ __device__ __forceinline__ void scan_tiles(const uint64_t *tile_mask, int n_tile
     __syncthreads();
     if (tid < 64) offsets_from_counts(s_cnt, s_off, E, bm, r, meta, pbt, split, tid);
     __syncthreads();
-    blocks_and_pads(s_off, s_cnt, E, bm, TK, r, sorted_tok, tid, nthreads);
+    blocks_and_pads(s_off, s_cnt, E, bm, PT, r, sorted_tok, tid, nthreads);
     if (do_scatter)
-        for (int p = tid; p < TK; p += nthreads)
-            scatter_pair(p, K, E, r, s_off, tile_base, tile_mask, pair_pos, sorted_tok);
+        for (int p = tid; p < PT; p += nthreads)
+            scatter_pair(p, K, TK, Er, S, r, s_off, tile_base, tile_mask, pair_pos, sorted_tok);
 }
 
 }  // namespace beam

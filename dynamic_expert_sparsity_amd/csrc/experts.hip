@@ -225,7 +225,7 @@ template <typename T_>
 __global__ __launch_bounds__(256) void up_generic(
     const T_ *__restrict__ x, const T_ *__restrict__ Wgu, const int32_t *__restrict__ block_expert,
     const int32_t *__restrict__ num_active, const int32_t *__restrict__ sorted_pairs,
-    T_ *__restrict__ h, int d, int I, int K, int TK, int bm) {
+    const int32_t *__restrict__ sorted_tok, T_ *__restrict__ h, int d, int I, int PT, int bm) {
     const int b = blockIdx.x;
     if (b >= num_active[3]) return;
     const int j = blockIdx.y * 256 + threadIdx.x;
@@ -235,9 +235,8 @@ __global__ __launch_bounds__(256) void up_generic(
     const T_ *wu = wg + (size_t)I * d;
     for (int i = 0; i < bm; ++i) {
         const int pos = b * bm + i;
-        const int pr = sorted_pairs[pos];
-        if (pr >= TK) break;  // pads only follow the valid entries
-        const T_ *xr = x + (size_t)(pr / K) * d;
+        if (sorted_pairs[pos] >= PT) break;  // pads only follow the valid entries
+        const T_ *xr = x + (size_t)sorted_tok[pos] * d;
         float a = 0.f, u = 0.f;
         for (int k = 0; k < d; ++k) {
             const float xv = elem<T_>::load(xr + k);
@@ -252,7 +251,7 @@ template <typename T_>
 __global__ __launch_bounds__(256) void down_generic(
     const T_ *__restrict__ Wdt, const T_ *__restrict__ h,
     const int32_t *__restrict__ block_expert, const int32_t *__restrict__ num_active,
-    const int32_t *__restrict__ sorted_pairs, T_ *__restrict__ o, int d, int I, int TK, int bm) {
+    const int32_t *__restrict__ sorted_pairs, T_ *__restrict__ o, int d, int I, int PT, int bm) {
     const int b = blockIdx.x;
     if (b >= num_active[3]) return;
     const int c = blockIdx.y * 256 + threadIdx.x;
@@ -261,7 +260,7 @@ __global__ __launch_bounds__(256) void down_generic(
     const T_ *w = Wdt + ((size_t)e * d + c) * I;
     for (int i = 0; i < bm; ++i) {
         const int pos = b * bm + i;
-        if (sorted_pairs[pos] >= TK) break;
+        if (sorted_pairs[pos] >= PT) break;
         const T_ *hr = h + (size_t)pos * I;
         float acc = 0.f;
         for (int k = 0; k < I; ++k) acc = fmaf(elem<T_>::load(hr + k), elem<T_>::load(w + k), acc);
@@ -270,18 +269,22 @@ __global__ __launch_bounds__(256) void down_generic(
 }
 
 // ---------------------------------------------------------------------------
-// Combine (Eq. 8): y_t = sum over k of g_hat[t,k] * o[pair_pos[t*K+k]], in
-// slot order, float accumulate; masked slots (pair_pos -1) are skipped, so a
-// token with no active slot gets exactly 0.
+// Combine (Eq. 8): y_t = the S shared experts' rows o[pair_pos[T*K + t*S + s]]
+// (weight 1), then sum over k of g_hat[t,k] * o[pair_pos[t*K+k]] in slot
+// order, float accumulate; masked slots (pair_pos -1) are skipped, so
+// without shared experts a token with no active slot gets exactly 0.
 // ---------------------------------------------------------------------------
 template <typename T_>
 __global__ __launch_bounds__(256) void combine_generic(const T_ *__restrict__ o,
                                                        const int32_t *__restrict__ pair_pos,
                                                        const float *__restrict__ g_hat,
-                                                       T_ *__restrict__ y, int d, int K) {
+                                                       T_ *__restrict__ y, int d, int K, int TK,
+                                                       int S) {
     const int t = blockIdx.x;
     for (int c = threadIdx.x; c < d; c += 256) {
         float acc = 0.f;
+        for (int q = 0; q < S; ++q)
+            acc += elem<T_>::load(o + (size_t)pair_pos[TK + t * S + q] * d + c);
         for (int k = 0; k < K; ++k) {
             const int pp = pair_pos[(size_t)t * K + k];
             if (pp >= 0) acc = fmaf(g_hat[(size_t)t * K + k], elem<T_>::load(o + (size_t)pp * d + c), acc);
@@ -294,12 +297,22 @@ __global__ __launch_bounds__(256) void combine_generic(const T_ *__restrict__ o,
 __global__ __launch_bounds__(256) void combine_bf16(const bf16_t *__restrict__ o,
                                                     const int32_t *__restrict__ pair_pos,
                                                     const float *__restrict__ g_hat,
-                                                    bf16_t *__restrict__ y, int d, int K) {
+                                                    bf16_t *__restrict__ y, int d, int K, int TK,
+                                                    int S) {
     const int t = blockIdx.x;
     for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
         float acc[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+        for (int sx = 0; sx < S; ++sx) {
+            const int pp = pair_pos[TK + t * S + sx];
+            const u32x4 v = ld16(o + (size_t)pp * d + c);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[2 * q] += __uint_as_float(v[q] << 16);
+                acc[2 * q + 1] += __uint_as_float(v[q] & 0xffff0000u);
+            }
+        }
         for (int k = 0; k < K; ++k) {
             const int pp = pair_pos[(size_t)t * K + k];
             if (pp < 0) continue;
@@ -590,14 +603,14 @@ hipError_t launch_expert_up(const Plan &p, const void *x, const void *W_gu, cons
         const hipError_t e = ring_attr((const void *)ring_bf16<false>);
         if (e != hipSuccess) return e;
         ring_bf16<false><<<ring_grid(), 512, RING_LDS, s>>>(
-            (const bf16_t *)x, (const bf16_t *)W_gu, w.pbt, w.meta + 4 * p.E, w.sorted_tok,
+            (const bf16_t *)x, (const bf16_t *)W_gu, w.pbt, w.meta + 4 * p.E2, w.sorted_tok,
             (bf16_t *)w.h, p.d, p.I, p.path == 1 ? 1 : 0);
     } else if (p.dtype == 1) {
         const unsigned grid = (unsigned)p.max_active * (unsigned)(p.I / 16);
 #define BEAM_UP(NWV, NKV)                                                                     \
     up_stream_bf16<NWV, NKV><<<grid, NWV * 64, 0, s>>>(                                      \
         (const bf16_t *)x, (const bf16_t *)W_gu, w.meta, r.num_active, w.sorted_tok,          \
-        (bf16_t *)w.h, p.d, p.I, p.path == 1 ? w.meta + 4 * p.E : nullptr)
+        (bf16_t *)w.h, p.d, p.I, p.path == 1 ? w.meta + 4 * p.E2 : nullptr)
         if (p.d % 256 == 0) {  // eight waves split d, d / 256 k-steps each
             switch (p.d / 256) {
                 case 1: BEAM_UP(8, 1); break;
@@ -616,7 +629,7 @@ hipError_t launch_expert_up(const Plan &p, const void *x, const void *W_gu, cons
         const dim3 grid((unsigned)p.n_blocks_cap, (p.I + 255) / 256);
         up_generic<float><<<grid, 256, 0, s>>>((const float *)x, (const float *)W_gu,
                                                r.block_expert, r.num_active, r.sorted_pairs,
-                                               (float *)w.h, p.d, p.I, p.K, p.T * p.K, p.bm);
+                                               w.sorted_tok, (float *)w.h, p.d, p.I, p.PT, p.bm);
     }
     return hipGetLastError();
 }
@@ -631,7 +644,7 @@ hipError_t launch_expert_down(const Plan &p, const void *W_dt, const Routing &r,
         const hipError_t e = ring_attr((const void *)ring_bf16<true>);
         if (e != hipSuccess) return e;
         ring_bf16<true><<<ring_grid(), 512, RING_LDS, s>>>(
-            (const bf16_t *)w.h, (const bf16_t *)W_dt, w.pbt, w.meta + 4 * p.E, w.sorted_tok,
+            (const bf16_t *)w.h, (const bf16_t *)W_dt, w.pbt, w.meta + 4 * p.E2, w.sorted_tok,
             (bf16_t *)w.o, p.I, p.d, p.path == 1 ? 1 : 0);
     } else if (p.dtype == 1) {
         const unsigned grid = (unsigned)p.max_active * (unsigned)(p.d / 64);
@@ -639,7 +652,7 @@ hipError_t launch_expert_down(const Plan &p, const void *W_dt, const Routing &r,
 #define BEAM_DOWN(NKV)                                                                        \
     down_stream_bf16<NKV><<<grid, 256, lds, s>>>((const bf16_t *)W_dt, (const bf16_t *)w.h,   \
                                                  w.meta, r.num_active, (bf16_t *)w.o, p.d,    \
-                                                 p.I, p.path == 1 ? w.meta + 4 * p.E : nullptr)
+                                                 p.I, p.path == 1 ? w.meta + 4 * p.E2 : nullptr)
         switch (p.I / 32) {  // k-steps per wave
             case 2: BEAM_DOWN(2); break;
             case 4: BEAM_DOWN(4); break;
@@ -656,7 +669,7 @@ hipError_t launch_expert_down(const Plan &p, const void *W_dt, const Routing &r,
         const dim3 grid((unsigned)p.n_blocks_cap, (p.d + 255) / 256);
         down_generic<float><<<grid, 256, 0, s>>>((const float *)W_dt, (const float *)w.h,
                                                  r.block_expert, r.num_active, r.sorted_pairs,
-                                                 (float *)w.o, p.d, p.I, p.T * p.K, p.bm);
+                                                 (float *)w.o, p.d, p.I, p.PT, p.bm);
     }
     return hipGetLastError();
 }
@@ -665,10 +678,10 @@ hipError_t launch_combine(const Plan &p, const Routing &r, const Work &w, void *
                           hipStream_t s) {
     if (p.dtype == 1)
         combine_bf16<<<p.T, 256, 0, s>>>((const bf16_t *)w.o, w.pair_pos, r.g_hat, (bf16_t *)y,
-                                         p.d, p.K);
+                                         p.d, p.K, p.T * p.K, p.S);
     else
         combine_generic<float><<<p.T, 256, 0, s>>>((const float *)w.o, w.pair_pos, r.g_hat,
-                                                   (float *)y, p.d, p.K);
+                                                   (float *)y, p.d, p.K, p.T * p.K, p.S);
     return hipGetLastError();
 }
 

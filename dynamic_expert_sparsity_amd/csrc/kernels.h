@@ -9,6 +9,10 @@ namespace beam {
 // Everything the launchers need, fixed on the host from the descriptor.
 struct Plan {
     int T, d, E, K, I;
+    int S;              // shared (always-on) experts, numbered E .. E+S-1
+    int E2;             // E + S: experts of the grouping and the expert kernels
+    int PT;             // T * (K + S): pair ids (routed t*K+k, then shared
+                        // T*K + t*S + s); also the pad value of sorted_pairs
     int dtype;          // 0 f32, 1 bf16
     int bm;             // block_m
     int path;           // 0 streaming (decode), 1 tiled (prefill)

@@ -272,10 +272,17 @@ __device__ __forceinline__ void select_group(int T, int E, int K, float thr, con
     }
 }
 
-// One workgroup per 64-token tile: the select, and the tile's token sets.
+// The token set of tile `tile` for a shared expert: every valid token.
+__device__ __forceinline__ unsigned long long tile_all(int tile, int T) {
+    const int n = T - tile * 64;
+    return n >= 64 ? ~0ull : ((1ull << n) - 1ull);
+}
+
+// One workgroup per 64-token tile: the select, and the tile's token sets for
+// the E routed and S shared experts ([tile][E + S]).
 template <int EJ, int LPT>
-__global__ __launch_bounds__(LPT * 64) void select_topk_mask(int T, int E, int K, float thr,
-                                                             Routing r,
+__global__ __launch_bounds__(LPT * 64) void select_topk_mask(int T, int E, int S, int K,
+                                                             float thr, Routing r,
                                                              uint64_t *__restrict__ tile_mask) {
     __shared__ unsigned long long tmask[256];
     const int tid = threadIdx.x;
@@ -284,14 +291,17 @@ __global__ __launch_bounds__(LPT * 64) void select_topk_mask(int T, int E, int K
     const int t_first = blockIdx.x * 64 + (tid >> 6) * (64 / LPT);
     if (t_first < T) select_group<EJ, LPT>(T, E, K, thr, r, tmask, nullptr, t_first, tid & 63);
     __syncthreads();
-    for (int e = tid; e < E; e += LPT * 64) tile_mask[(size_t)blockIdx.x * E + e] = tmask[e];
+    const int E2 = E + S;
+    for (int e = tid; e < E2; e += LPT * 64)
+        tile_mask[(size_t)blockIdx.x * E2 + e] = e < E ? tmask[e] : tile_all(blockIdx.x, T);
 }
 
 // The grouping of a batch of tiles by one workgroup (and the pair positions
 // when the batch is small).
 __global__ __launch_bounds__(1024) void compact_tiles(const uint64_t *__restrict__ tile_mask,
-                                                      int n_tiles, int E, int bm, int K, int TK,
-                                                      Routing r, int32_t *__restrict__ tile_base,
+                                                      int n_tiles, int E, int S, int bm, int K,
+                                                      int TK, Routing r,
+                                                      int32_t *__restrict__ tile_base,
                                                       int32_t *__restrict__ pair_pos,
                                                       int32_t *__restrict__ meta,
                                                       int32_t *__restrict__ sorted_tok,
@@ -300,14 +310,15 @@ __global__ __launch_bounds__(1024) void compact_tiles(const uint64_t *__restrict
     __shared__ int s_part[1024];
     __shared__ int s_cnt[256];
     __shared__ int s_off[257];
-    scan_tiles(tile_mask, n_tiles, E, bm, K, TK, r, tile_base, pair_pos, meta, sorted_tok,
+    scan_tiles(tile_mask, n_tiles, E, S, bm, K, TK, r, tile_base, pair_pos, meta, sorted_tok,
                pbt, fuse_scatter != 0, split, threadIdx.x, 1024, s_part, s_cnt, s_off);
 }
 
 // A small batch (T <= 64, one tile) in one workgroup: select, counts,
-// offsets, lists and pair positions; the token sets and masked ids stay in LDS.
+// offsets, lists and pair positions of the E routed and S shared experts;
+// the token sets and masked ids stay in LDS.
 template <int EJ, int LPT>
-__global__ __launch_bounds__(1024) void route_small(int T, int E, int K, float thr, int bm,
+__global__ __launch_bounds__(1024) void route_small(int T, int E, int S, int K, float thr, int bm,
                                                     Routing r, int32_t *__restrict__ pair_pos,
                                                     int32_t *__restrict__ meta,
                                                     int32_t *__restrict__ sorted_tok,
@@ -318,17 +329,18 @@ __global__ __launch_bounds__(1024) void route_small(int T, int E, int K, float t
     __shared__ int s_off[257];
     constexpr int TPW = 64 / LPT;  // tokens per wavefront
     const int tid = threadIdx.x;
+    const int E2 = E + S;
     if (tid < E) tmask[tid] = 0ull;
     __syncthreads();
     for (int t_first = (tid >> 6) * TPW; t_first < T; t_first += 16 * TPW)
         select_group<EJ, LPT>(T, E, K, thr, r, tmask, s_mid, t_first, tid & 63);
     __syncthreads();
-    if (tid < E) s_cnt[tid] = __popcll(tmask[tid]);
+    if (tid < E2) s_cnt[tid] = tid < E ? __popcll(tmask[tid]) : T;
     __syncthreads();
-    if (tid < 64) offsets_from_counts(s_cnt, s_off, E, bm, r, meta, pbt, split, tid);
+    if (tid < 64) offsets_from_counts(s_cnt, s_off, E2, bm, r, meta, pbt, split, tid);
     __syncthreads();
-    const int TK = T * K;
-    blocks_and_pads(s_off, s_cnt, E, bm, TK, r, sorted_tok, tid, 1024);
+    const int TK = T * K, PT = TK + T * S;
+    blocks_and_pads(s_off, s_cnt, E2, bm, PT, r, sorted_tok, tid, 1024);
     for (int p = tid; p < TK; p += 1024) {
         const int e = s_mid[p];
         if (e < 0) {
@@ -336,21 +348,25 @@ __global__ __launch_bounds__(1024) void route_small(int T, int E, int K, float t
             continue;
         }
         const int t = p / K;
-        place_pair(p, e, s_off[e] + __popcll(tmask[e] & ((1ull << t) - 1ull)), K, r, pair_pos,
+        place_pair(p, t, s_off[e] + __popcll(tmask[e] & ((1ull << t) - 1ull)), r, pair_pos,
                    sorted_tok);
+    }
+    for (int q = tid; q < T * S; q += 1024) {  // shared experts: every token, in order
+        const int t = q / S, sx = q - t * S;
+        place_pair(TK + q, t, s_off[E + sx] + t, r, pair_pos, sorted_tok);
     }
 }
 
 template <int EJ, int LPT>
 static void launch_select_t(const Plan &p, const Routing &r, const Work &w, hipStream_t s) {
     if (p.T <= 64) {
-        route_small<EJ, LPT><<<1, 1024, 0, s>>>(p.T, p.E, p.K, p.thr, p.bm, r, w.pair_pos, w.meta,
-                                               w.sorted_tok, w.pbt, p.split);
+        route_small<EJ, LPT><<<1, 1024, 0, s>>>(p.T, p.E, p.S, p.K, p.thr, p.bm, r, w.pair_pos,
+                                               w.meta, w.sorted_tok, w.pbt, p.split);
     } else {
-        select_topk_mask<EJ, LPT><<<p.n_tiles, LPT * 64, 0, s>>>(p.T, p.E, p.K, p.thr, r,
+        select_topk_mask<EJ, LPT><<<p.n_tiles, LPT * 64, 0, s>>>(p.T, p.E, p.S, p.K, p.thr, r,
                                                                w.tile_mask);
-        compact_tiles<<<1, 1024, 0, s>>>(w.tile_mask, p.n_tiles, p.E, p.bm, p.K, p.T * p.K, r,
-                                         w.tile_base, w.pair_pos, w.meta, w.sorted_tok, w.pbt,
+        compact_tiles<<<1, 1024, 0, s>>>(w.tile_mask, p.n_tiles, p.E, p.S, p.bm, p.K, p.T * p.K,
+                                         r, w.tile_base, w.pair_pos, w.meta, w.sorted_tok, w.pbt,
                                          p.fuse_scatter, p.split);
     }
 }

@@ -39,7 +39,7 @@ from dataclasses import dataclass
 
 import torch
 
-__all__ = ["LayerShape", "SHAPES", "make_layer", "make_router", "make_tokens", "with_mask_bias",
+__all__ = ["LayerShape", "SHAPES", "N_SHARED", "make_layer", "make_router", "make_tokens", "with_mask_bias",
            "workload_name"]
 
 
@@ -59,7 +59,14 @@ SHAPES = {
     "qwen3": LayerShape(2048, 128, 8, 768, torch.bfloat16),
     # larger layer: d=4096, 128 experts, top-8, intermediate 1536
     "large": LayerShape(4096, 128, 8, 1536, torch.bfloat16),
+    # DeepSeekV2-Lite-shaped layer: 64 routed experts, top-6, 2 shared experts
+    "dsv2lite": LayerShape(2048, 64, 6, 1408, torch.bfloat16),
+    # Qwen1.5-MoE-A2.7B-shaped layer: 60 routed experts, top-4, 4 shared experts
+    "qwen15": LayerShape(2048, 60, 4, 1408, torch.bfloat16),
 }
+
+# shared (always-on) experts of each shape
+N_SHARED = {"tiny": 0, "qwen3": 0, "large": 0, "dsv2lite": 2, "qwen15": 4}
 
 _TID = {"x": 1, "W_gate": 2, "W_mask": 3, "W_gu": 4, "W_dt": 5, "perm": 6,
         "tokperm": 7, "Ws_gu": 8, "Ws_dt": 9}

@@ -30,10 +30,11 @@
  *   x       [T, d]
  *   W_gate  [E, d]      one row per expert (the transpose of the paper's
  *   W_mask  [E, d]      R in R^{d x N} and W_m in R^{d_h x N}; nn.Linear layout)
- *   W_gu    [E, 2I, d]  rows 0..I-1: gate projection (Eq. 3 "W_gate^(i)"),
+ *   W_gu    [E+S, 2I, d] rows 0..I-1: gate projection (Eq. 3 "W_gate^(i)"),
  *                       rows I..2I-1: up projection; each row is one
- *                       intermediate unit
- *   W_dt    [E, d, I]   down projection, one row per output channel
+ *                       intermediate unit; experts 0..E-1 routed, E..E+S-1
+ *                       the S = desc.n_shared shared experts
+ *   W_dt    [E+S, d, I] down projection, one row per output channel
  *   y       [T, d]
  */
 #ifndef BEAM_MOE_H
@@ -50,7 +51,7 @@ extern "C" {
 /* status codes */
 #define BEAM_OK            0
 #define BEAM_EINVAL       (-1) /* null/misaligned pointer, bad sizes, K > E ...   */
-#define BEAM_EUNSUPPORTED (-2) /* valid but outside kernel coverage: E > 256,
+#define BEAM_EUNSUPPORTED (-2) /* valid but outside kernel coverage: E+S > 256,
                                   K > 16, or (bf16) d % 128, I % 64, I > 2040     */
 #define BEAM_EWORKSPACE   (-3) /* workspace too small                              */
 #define BEAM_EHIP         (-4) /* a HIP launch failed                              */
@@ -94,11 +95,18 @@ typedef struct beam_moe_desc {
     uint32_t flags;    /* BEAM_FORCE_*                                         */
     float    tau;      /* mask threshold on sigmoid(z); 0 means 0.5 (Eq. 6).
                           Evaluated exactly as z >= ln(tau / (1 - tau)).       */
-    int32_t  reserved[3]; /* must be 0                                         */
+    int32_t  n_shared; /* S >= 0 always-on shared experts (E + S <= 256): applied
+                          to every token with weight 1, never masked, added
+                          to the routed sum; their weights follow the routed
+                          experts' in W_gu and W_dt (news article on the
+                          paper, sections 5-6: DeepSeek / Qwen1.5-MoE shapes) */
+    int32_t  reserved[2]; /* must be 0                                         */
 } beam_moe_desc;
 
 /* Routing outputs (all device pointers, caller-owned; sizes from
- * beam_moe_query).  A "pair" is p = t*K + k. */
+ * beam_moe_query).  A "pair" is p = t*K + k for the routed slot k of token t,
+ * and p = T*K + t*S + s for shared expert E + s (S = desc.n_shared); the
+ * grouping fields below cover the E + S experts. */
 typedef struct beam_moe_routing {
     float   *gate_logits;    /* [T, E]  r (fp32 accumulate)                      */
     float   *mask_logits;    /* [T, E]  z                                        */
@@ -107,17 +115,17 @@ typedef struct beam_moe_routing {
     uint8_t *mask;           /* [T, K]  m in {0, 1} (Eq. 6)                      */
     float   *g_hat;          /* [T, K]  g * m (Eq. 7)                            */
     int32_t *masked_ids;     /* [T, K]  topk_ids, or -1 where m = 0              */
-    int32_t *expert_counts;  /* [E]     active pairs per expert                  */
-    int32_t *expert_offsets; /* [E+1]   exclusive scan of counts rounded up to
+    int32_t *expert_counts;  /* [E+S]   active pairs per expert (shared: T)      */
+    int32_t *expert_offsets; /* [E+S+1] exclusive scan of counts rounded up to
                                         block_m                                  */
     int32_t *sorted_pairs;   /* [cap]   per expert: its pair ids ascending, then
-                                        the pad value T*K up to a multiple of
-                                        block_m; entries >= num_padded unused    */
+                                        the pad value T*(K+S) up to a multiple
+                                        of block_m; entries >= num_padded unused */
     int32_t *block_expert;   /* [cap/block_m] expert of each block_m block       */
-    int32_t *active_experts; /* [E]     experts with count >= 1, ascending;
+    int32_t *active_experts; /* [E+S]   experts with count >= 1, ascending;
                                         entries >= n_active_experts unused       */
-    int32_t *num_active;     /* [4]     {P = active pairs, num_padded,
-                                         n_active_experts, n_blocks}             */
+    int32_t *num_active;     /* [4]     {P = active pairs (shared included),
+                                         num_padded, n_active_experts, n_blocks} */
 } beam_moe_routing;
 
 /* Sizes for a descriptor (host only, enqueues nothing). */

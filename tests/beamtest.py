@@ -56,10 +56,10 @@ def gpu_routing_host(R):
     }
 
 
-def check_routing_exact(G, K, block_m, tau=0.5):
+def check_routing_exact(G, K, block_m, tau=0.5, n_shared=0):
     """Every discrete routing output must equal the oracle's decisions on the
     GPU's own float32 logits, bit for bit; g and g_hat to float32 rounding."""
-    O = oracle.route_from_logits(G["gate_logits"], G["mask_logits"], K, block_m, tau)
+    O = oracle.route_from_logits(G["gate_logits"], G["mask_logits"], K, block_m, tau, n_shared)
     for k in ROUTE_KEYS_EXACT:
         if k == "num_active":
             want = np.array([O["num_active"][0], O["num_active"][1], len(O["active_experts"]),
@@ -91,15 +91,22 @@ def rel_l2(a, b):
 
 
 def check_y(y, L, K, O, tol, tokens=None):
-    """y against the oracle's Eq. 8 on the same routing decisions."""
+    """y against the oracle's Eq. 8 on the same routing decisions (plus the
+    shared experts when L has them)."""
     rows = np.arange(y.shape[0]) if tokens is None else np.asarray(tokens)
+    shared = None
+    if "Ws_gu" in L and L["Ws_gu"].shape[0] > 0:
+        n = L["Ws_gu"].shape[0]
+        shared = ([L["Ws_gu"][s].float().cpu().numpy() for s in range(n)],
+                  [L["Ws_dt"][s].float().cpu().numpy() for s in range(n)])
     ref = oracle.forward(host(L["x"]), None, None, ExpertView(L["W_gu"]), ExpertView(L["W_dt"]),
-                         K, routing=O, tokens=rows)
+                         K, routing=O, tokens=rows, shared=shared)
     err = rel_l2(y[rows], ref)
     assert err <= tol, f"y rel-L2 {err:.3e} > {tol}"
-    # tokens with no active slot are exactly zero
-    dead = rows[np.asarray(O["mask"])[rows].sum(axis=1) == 0]
-    assert np.all(y[dead] == 0.0)
+    if shared is None:
+        # tokens with no active slot are exactly zero
+        dead = rows[np.asarray(O["mask"])[rows].sum(axis=1) == 0]
+        assert np.all(y[dead] == 0.0)
     return err
 
 
