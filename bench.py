@@ -20,7 +20,8 @@ bf16 MFMA rate, the same kernels with the mask forced all-ones (W_mask = 0,
 plain Top-K), a sweep over the decode batch sizes, the prefill runs (keep
 0.15 / 0.3 / 0.5 / 1.0 at T = 2048 and 8192, and the skewed T = 16384 load),
 a stack of 48 distinct layers at T = 64 under the skewed load (eager and as
-one replayed HIP graph), the d=4096/I=1536 layer (decode T = 1 and 64,
+one replayed HIP graph), a DeepSeekV2-Lite-shaped layer with two always-on
+shared experts (decode, masked and all-ones), the d=4096/I=1536 layer (decode T = 1 and 64,
 prefill T = 4096, keep 0.15 and 0.5), and the fp64 oracle timed on this
 host's cores on a bounded sample of the headline workload.
 """
@@ -82,6 +83,9 @@ def parse():
     ap.add_argument("--no-stack", dest="stack", action="store_false")
     ap.add_argument("--stack-T", type=int, default=64)
     ap.add_argument("--stack-steps", type=int, default=20)
+    ap.add_argument("--shared", action="store_true", default=True,
+                    help="also measure the DeepSeekV2-Lite-shaped layer with 2 shared experts")
+    ap.add_argument("--no-shared", dest="shared", action="store_false")
     ap.add_argument("--large", action="store_true", default=True,
                     help="also measure the d=4096/I=1536 layer (decode T=1, 64; prefill 4096)")
     ap.add_argument("--no-large", dest="large", action="store_false")
@@ -420,6 +424,11 @@ def main():
             f"{stack['eager']['ms_per_step']:.3f} ms, graph {stack['graph']['ms_per_step']:.3f} ms "
             f"per step")
 
+    # ---- shared experts: DeepSeekV2-Lite-shaped layer ------------------------
+    shared = None
+    if args.shared and not args.only_headline:
+        shared = run_shared(B, synth, dev, measure, args)
+
     prefill_out = [] if args.only_headline else run_prefill()
 
     # ---- CPU baseline: the fp64 oracle on this host's cores ---------------
@@ -469,6 +478,7 @@ def main():
         "sweep": sweep_out,
         "prefill": prefill_out,
         "stack": stack,
+        "shared": shared,
         "large": large,
         "cpu_baseline": cpu,
     }
@@ -545,6 +555,45 @@ def run_stack(B, synth, sets, shape, dev, T, steps, dims):
            "bytes_per_step": byts, "eager": eager, "graph": graph}
     del g, Ls
     return out
+
+
+def run_shared(B, synth, dev, measure, args):
+    """The DeepSeekV2-Lite-shaped layer (d=2048, 64 routed experts, top-6,
+    I=1408, 2 always-on shared experts): decode T = 1, 32, 256 at mask bias
+    -1.04 and with the all-ones mask (the shared experts run in both)."""
+    import torch
+
+    shp = synth.SHAPES["dsv2lite"]
+    S = synth.N_SHARED["dsv2lite"]
+    d, E, K, I = shp.d, shp.E, shp.K, shp.I
+    per_set = (E + S) * 3 * d * I * 2
+    free, _ = torch.cuda.mem_get_info()
+    n = max(1, min(24, int(0.4 * free // per_set)))
+    log(f"shared-expert layer: drawing {n} weight sets ({n * per_set / 1e9:.1f} GB)")
+    sets = []
+    for s in range(n):
+        L = synth.make_layer(shp, 256, seed=0, layer=400 + s, mask_bias=-1.04, n_shared=S,
+                             device=dev)
+        L["W_gu"] = torch.cat([L.pop("W_gu"), L.pop("Ws_gu")]).contiguous()
+        L["W_dt"] = torch.cat([L.pop("W_dt"), L.pop("Ws_dt")]).contiguous()
+        sets.append(L)
+    zeros = torch.zeros_like(sets[0]["W_mask"])
+    out = []
+    for T in (1, 32, 256):
+        row = {"T": T}
+        for kind in ("masked", "allones"):
+            Ls = [(B.MoELayer(L["W_gate"], zeros if kind == "allones" else L["W_mask"],
+                              L["W_gu"], L["W_dt"], K), L["x"][:T].contiguous()) for L in sets]
+            m = measure(Ls, T, args.sweep_steps, 10, dims=(d, E, K, I))
+            row[kind] = {k: _r(v) for k, v in m.items() if not k.startswith("_")}
+            del Ls
+        row["speedup_vs_allones"] = round(row["allones"]["ms_per_step"] /
+                                          row["masked"]["ms_per_step"], 3)
+        out.append(row)
+        log(f"shared-expert layer T={T}: masked {row['masked']['ms_per_step']*1e3:.1f} us, "
+            f"all-ones {row['allones']['ms_per_step']*1e3:.1f} us")
+    del sets
+    return {"workload": f"d{d}-E{E}+{S}shared-K{K}-I{I}-bf16", "weight_sets": n, "runs": out}
 
 
 def run_large(B, synth, dev, measure, prefill_entry, args):

@@ -40,6 +40,12 @@ Readings of points the pages leave open (each is also listed in the design doc):
   T1  (threshold variants, the ablation over tau in the news article section
       8) tau != 0.5 is evaluated as z >= ln(tau / (1 - tau)), the exact
       preimage of sigmoid >= tau.
+  B1  (training, paper section 3.3 and news article section 4) the
+      binarisation m = [m_hat >= 0.5] is passed by the straight-through
+      estimator: dL/dm_hat = dL/dm; the sparsity term is
+      L_sp = beta * sum_t sum_k m_hat[t, id_k] over the K candidates of every
+      token (a plain sum; any normalisation is folded into beta); dL/dm
+      follows from Eq. 7-8 as g_k * dL/dg_hat_k.
   S1  (shared experts, news article sections 5 and 6: models with always-on
       shared experts keep running them for a token whose routed slots are
       all masked) a shared expert is a SwiGLU expert of the routed experts'
@@ -65,6 +71,7 @@ __all__ = [
     "swiglu_expert",
     "forward",
     "routing_stats",
+    "mask_backward",
 ]
 
 
@@ -361,3 +368,44 @@ def forward(x, W_gate, W_mask, W_gu, W_dt, K: int, routing: dict | None = None,
     for k in range(ids.shape[1]):
         y += contrib[:, k]
     return y
+
+
+# ---------------------------------------------------------------------------
+# Mask-router backward: straight-through estimator and sparsity gradient
+# (paper section 3.3, "straight-through estimation"; news article section 4)
+# ---------------------------------------------------------------------------
+def mask_backward(x, W_mask, ids, g, m, z, slot_grad, beta: float) -> dict:
+    """Gradients of the mask router for one layer call (reading B1).
+
+    x [T, d], W_mask [E, d]; ids, g, m [T, K]: the forward's Top-K ids, the
+    softmax weights g and the hard mask m; z [T, E]: mask logits;
+    slot_grad [T, K]: dL/dg_hat (for y = sum_k g_hat_k E_k(x), this is
+    <dL/dy, E_{id_k}(x)>, also for masked slots).  Returns float64:
+      dz [T, E]        dL/dz: (g_k * slot_grad_k + beta) * s (1 - s) at each
+                       candidate id_k, s = sigmoid(z); 0 elsewhere
+      dW_mask [E, d]   dz^T x
+      dx [T, d]        dz W_mask (the mask router's share of dL/dx)
+      d_gate [T, E]    dL/dr through the softmax over the kept logits (Eq. 4)
+                       with dL/dg_k = m_k * slot_grad_k; 0 off the Top-K
+    """
+    x = _f64(x)
+    W = _f64(W_mask)
+    ids = np.asarray(ids)
+    g = _f64(g)
+    m = _f64(m)
+    z = _f64(z)
+    sg = _f64(slot_grad)
+    T, K = ids.shape
+    E = W.shape[0]
+    dz = np.zeros((T, E))
+    d_gate = np.zeros((T, E))
+    for t in range(T):
+        dg = m[t] * sg[t]                       # dL/dg_k through g_hat = g * m
+        inner = float(np.dot(g[t], dg))
+        for k in range(K):
+            e = int(ids[t, k])
+            s = 1.0 / (1.0 + math.exp(-z[t, e]))
+            dm_hat = g[t, k] * sg[t, k] + beta  # STE: dL/dm_hat = dL/dm, plus L_sp
+            dz[t, e] += dm_hat * s * (1.0 - s)
+            d_gate[t, e] += g[t, k] * (dg[k] - inner)   # softmax Jacobian
+    return {"dz": dz, "dW_mask": dz.T @ x, "dx": dz @ W, "d_gate": d_gate}

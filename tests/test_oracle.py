@@ -478,3 +478,86 @@ def test_stats_binomial_closed_form():
     for j in range(K + 1):
         pj = math.comb(K, j) * p ** j * (1 - p) ** (K - j)
         assert abs(S["active_hist"][j] / T - pj) <= 4 * math.sqrt(pj * (1 - pj) / T) + 1e-3, j
+
+
+# ---------------------------------------------------------------------------
+# Mask-router backward (straight-through estimator + sparsity term).  With
+# g, the Top-K ids and the slot gradients held fixed, the STE gradient is the
+# exact gradient of the smooth surrogate in which the hard mask is replaced
+# by m_hat = sigmoid(z) (the backward treats m as m_hat); central finite
+# differences of that surrogate, written here from its definition, pin it.
+# ---------------------------------------------------------------------------
+def _bwd_case(seed, T=6, E=7, K=3, d=5):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, d))
+    Wg = rng.standard_normal((E, d))
+    Wm = 0.5 * rng.standard_normal((E, d))
+    R = oracle.route(x, Wg, Wm, K)
+    sg = rng.standard_normal((T, K))
+    return x, Wg, Wm, R, sg
+
+
+def _sigmoid(v):
+    return 1.0 / (1.0 + np.exp(-v))
+
+
+def _surrogate_mask(x_z, Wm, ids, g, sg, beta):
+    z = x_z @ Wm.T
+    zk = np.take_along_axis(z, ids, axis=1)
+    return float(np.sum((g * sg + beta) * _sigmoid(zk)))
+
+
+def _surrogate_gate(r, ids, m, sg):
+    kept = np.take_along_axis(r, ids, axis=1)
+    w = np.exp(kept - kept.max(axis=1, keepdims=True))
+    g = w / w.sum(axis=1, keepdims=True)
+    return float(np.sum(g * m * sg))
+
+
+@pytest.mark.parametrize("seed,beta", [(20, 0.0), (21, 0.3), (22, -0.7)])
+def test_mask_backward_finite_differences(seed, beta):
+    x, Wg, Wm, R, sg = _bwd_case(seed)
+    ids, g, m = R["topk_ids"], R["topk_weights"], R["mask"]
+    G = oracle.mask_backward(x, Wm, ids, g, m, R["mask_logits"], sg, beta)
+    h = 1e-6
+    for (e, c) in [(0, 0), (3, 2), (6, 4), (int(ids[0, 0]), 1)]:
+        P, M = Wm.copy(), Wm.copy()
+        P[e, c] += h
+        M[e, c] -= h
+        fd = (_surrogate_mask(x, P, ids, g, sg, beta) - _surrogate_mask(x, M, ids, g, sg, beta)) / (2 * h)
+        assert abs(fd - G["dW_mask"][e, c]) <= 1e-7 * max(1.0, abs(fd)), (e, c)
+    for (t, c) in [(0, 0), (2, 3), (5, 4)]:
+        P, M = x.copy(), x.copy()
+        P[t, c] += h
+        M[t, c] -= h
+        fd = (_surrogate_mask(P, Wm, ids, g, sg, beta) - _surrogate_mask(M, Wm, ids, g, sg, beta)) / (2 * h)
+        assert abs(fd - G["dx"][t, c]) <= 1e-7 * max(1.0, abs(fd)), (t, c)
+    r = R["gate_logits"]
+    for t in (0, 4):
+        for e in range(r.shape[1]):
+            P, M = r.copy(), r.copy()
+            P[t, e] += h
+            M[t, e] -= h
+            fd = (_surrogate_gate(P, ids, m, sg) - _surrogate_gate(M, ids, m, sg)) / (2 * h)
+            assert abs(fd - G["d_gate"][t, e]) <= 1e-7 * max(1.0, abs(fd)), (t, e)
+
+
+def test_mask_backward_special_cases():
+    x, Wg, Wm, R, sg = _bwd_case(23)
+    ids, g, m = R["topk_ids"], R["topk_weights"], R["mask"]
+    T, E = R["mask_logits"].shape
+    # no upstream gradient and no sparsity term: nothing flows
+    G = oracle.mask_backward(x, Wm, ids, g, m, R["mask_logits"], np.zeros_like(sg), 0.0)
+    assert not G["dz"].any() and not G["dW_mask"].any() and not G["d_gate"].any()
+    # z = 0 (the paper's zero-initialised mask router): sigmoid' = 1/4, so the
+    # sparsity term alone gives dz = beta / 4 at every candidate, 0 elsewhere
+    z0 = np.zeros((T, E))
+    G = oracle.mask_backward(x, np.zeros_like(Wm), ids, g, np.ones_like(m), z0,
+                             np.zeros_like(sg), 2.0)
+    want = np.zeros((T, E))
+    for t in range(T):
+        want[t, ids[t]] = 0.5
+    np.testing.assert_array_equal(G["dz"], want)
+    # the gate gradient sums to zero over each token's kept logits (softmax)
+    G = oracle.mask_backward(x, Wm, ids, g, m, R["mask_logits"], sg, 0.1)
+    np.testing.assert_allclose(G["d_gate"].sum(axis=1), 0.0, atol=1e-14)
