@@ -60,7 +60,8 @@ class Routing(ctypes.Structure):
 class Sizes(ctypes.Structure):
     _fields_ = [("workspace_bytes", ctypes.c_size_t), ("route_workspace_bytes", ctypes.c_size_t),
                 ("cap", ctypes.c_int64), ("n_blocks_cap", ctypes.c_int64),
-                ("block_m", ctypes.c_int32), ("path", ctypes.c_int32)]
+                ("block_m", ctypes.c_int32), ("path", ctypes.c_int32),
+                ("mask_backward_workspace_bytes", ctypes.c_size_t)]
 
 
 _lib = None
@@ -88,6 +89,9 @@ def lib() -> ctypes.CDLL:
         L.beam_moe_forward_ex.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, vp, vp, vp,
                                           ctypes.POINTER(Routing), vp, sz, vp, vp]
         L.beam_moe_forward_ex.restype = ctypes.c_int
+        L.beam_moe_mask_backward.argtypes = [ctypes.POINTER(Desc), vp, vp, ctypes.POINTER(Routing),
+                                             vp, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp]
+        L.beam_moe_mask_backward.restype = ctypes.c_int
         L.beam_moe_stats.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Routing), vp, vp, vp,
                                      vp]
         L.beam_moe_stats.restype = ctypes.c_int
@@ -175,7 +179,8 @@ def query(desc: Desc) -> dict:
     s = Sizes()
     _check(lib().beam_moe_query(ctypes.byref(desc), ctypes.byref(s)))
     return {"workspace_bytes": s.workspace_bytes, "route_workspace_bytes": s.route_workspace_bytes,
-            "cap": s.cap, "n_blocks_cap": s.n_blocks_cap, "block_m": s.block_m, "path": s.path}
+            "cap": s.cap, "n_blocks_cap": s.n_blocks_cap, "block_m": s.block_m, "path": s.path,
+            "mask_backward_workspace_bytes": s.mask_backward_workspace_bytes}
 
 
 def alloc_routing(desc: Desc, sizes: dict, device) -> dict:
@@ -278,6 +283,32 @@ class MoELayer:
         return self.y, self.routing
 
     __call__ = forward
+
+    def mask_backward(self, x, slot_grad, beta=0.0, want_dW=True, want_dx=True,
+                      want_d_gate=True, stream=None) -> dict:
+        """beam_moe_mask_backward on this layer's last routing (of x): the
+        mask router's gradients (float32 tensors; None where not asked for).
+        slot_grad [T, K] float32: dL/dg_hat."""
+        _gpu_tensor("x", x, self.dtype)
+        T = x.shape[0]
+        if T != self._T:
+            raise ValueError("call the layer on x first (the backward reads its routing)")
+        _gpu_tensor("slot_grad", slot_grad, torch.float32, (T, self.K))
+        dev = x.device
+        f32 = torch.float32
+        dz = torch.empty((T, self.E), dtype=f32, device=dev)
+        dW = torch.empty((self.E, self.d), dtype=f32, device=dev) if want_dW else None
+        dx = torch.empty((T, self.d), dtype=f32, device=dev) if want_dx else None
+        dg = torch.empty((T, self.E), dtype=f32, device=dev) if want_d_gate else None
+        nb = max(self.sizes["mask_backward_workspace_bytes"], 256)
+        if getattr(self, "_bws", None) is None or self._bws.numel() < nb:
+            self._bws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+        _check(lib().beam_moe_mask_backward(
+            ctypes.byref(self.desc), x.data_ptr(), self.W_mask.data_ptr(), ctypes.byref(self._rs),
+            slot_grad.data_ptr(), float(beta), dz.data_ptr(), ptr(dW), ptr(dx), ptr(dg),
+            self._bws.data_ptr(), self._bws.numel(), _stream_ptr(stream)))
+        return {"dz": dz, "dW_mask": dW, "dx": dx, "d_gate": dg}
 
     def stats(self, counters: "RoutingStats", stream=None):
         """Add the statistics of this layer's last routing to `counters`."""

@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbeam_moe.so")
-SOURCES = ["router.hip", "compact.hip", "experts.hip", "gemm.hip", "stats.hip", "api.hip"]
+SOURCES = ["router.hip", "compact.hip", "experts.hip", "gemm.hip", "stats.hip", "backward.hip", "api.hip"]
 PEAK_LIB = os.path.join(PKG, "libbeam_peak.so")
 PEAK_SOURCES = ["peak.hip"]
 

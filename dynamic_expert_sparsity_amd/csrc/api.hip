@@ -193,6 +193,7 @@ int beam_moe_query(const beam_moe_desc *desc, beam_moe_sizes *out) {
     out->n_blocks_cap = p.n_blocks_cap;
     out->block_m = p.bm;
     out->path = p.path;
+    out->mask_backward_workspace_bytes = mask_backward_plan(p).bytes;
     return BEAM_OK;
 }
 
@@ -248,6 +249,45 @@ int beam_moe_forward(const beam_moe_desc *desc, const void *x, const void *W_gat
                      const beam_moe_routing *out, void *ws, size_t ws_bytes, hipStream_t stream) {
     return beam_moe_forward_ex(desc, x, W_gate, W_mask, W_gu, W_dt, y, out, ws, ws_bytes, stream,
                                nullptr);
+}
+
+int beam_moe_mask_backward(const beam_moe_desc *desc, const void *x, const void *W_mask,
+                           const beam_moe_routing *routing, const float *slot_grad, float beta,
+                           float *d_mask_logits, float *dW_mask, float *dx,
+                           float *d_gate_logits, void *ws, size_t ws_bytes, hipStream_t stream) {
+    Plan p;
+    int rc = make_plan(desc, p);
+    if (rc) return rc;
+    if (p.T == 0) return BEAM_OK;
+    if (!aligned(x, 16)) return fail(BEAM_EINVAL, "x is NULL or not 16-byte aligned");
+    if (!aligned(W_mask, 16)) return fail(BEAM_EINVAL, "W_mask is NULL or not 16-byte aligned");
+    if (!routing) return fail(BEAM_EINVAL, "routing struct is NULL");
+    if (!aligned(routing->topk_ids, 4) || !aligned(routing->topk_weights, 4) || !routing->mask ||
+        !aligned(routing->mask_logits, 4))
+        return fail(BEAM_EINVAL,
+                    "routing.topk_ids, topk_weights, mask and mask_logits must be set");
+    if (!aligned(slot_grad, 4)) return fail(BEAM_EINVAL, "slot_grad is NULL or misaligned");
+    if (!aligned(d_mask_logits, 4)) return fail(BEAM_EINVAL, "d_mask_logits is NULL or misaligned");
+    if (dW_mask && !aligned(dW_mask, 16)) return fail(BEAM_EINVAL, "dW_mask is not 16-byte aligned");
+    if (dx && !aligned(dx, 16)) return fail(BEAM_EINVAL, "dx is not 16-byte aligned");
+    if (d_gate_logits && !aligned(d_gate_logits, 4))
+        return fail(BEAM_EINVAL, "d_gate_logits is not 4-byte aligned");
+    if (!std::isfinite(beta)) return fail(BEAM_EINVAL, "beta is not finite");
+    const BwdPlan b = mask_backward_plan(p);
+    if (b.bytes > 0 && !aligned(ws, 16))
+        return fail(BEAM_EINVAL, "workspace is NULL or not 16-byte aligned");
+    if (ws_bytes < b.bytes)
+        return fail(BEAM_EWORKSPACE, "workspace has %zu bytes, the backward needs %zu", ws_bytes,
+                    b.bytes);
+    Routing r{};
+    r.topk_ids = routing->topk_ids;
+    r.topk_weights = routing->topk_weights;
+    r.mask = routing->mask;
+    r.mask_logits = routing->mask_logits;
+    BEAM_TRY(launch_mask_backward(p, b, x, W_mask, r, slot_grad, beta, d_mask_logits, dW_mask, dx,
+                                  d_gate_logits, ws, stream),
+             "mask backward");
+    return BEAM_OK;
 }
 
 int beam_moe_stats(const beam_moe_desc *desc, const beam_moe_routing *routing,

@@ -76,6 +76,17 @@ hipError_t launch_expert_down(const Plan &p, const void *W_dt, const Routing &r,
                               const Work &w, hipStream_t s);
 hipError_t launch_combine(const Plan &p, const Routing &r, const Work &w, void *y,
                           hipStream_t s);
+// mask-router backward: workspace layout and launches
+struct BwdPlan {
+    int T_pad, E_pad;       // tokens rounded up to the dW chunk, experts to 16
+    int n_split;            // token ranges of the dW contraction
+    int t_per_split;        // tokens per range (a multiple of the chunk)
+    size_t off_dzT, off_part, bytes;
+};
+BwdPlan mask_backward_plan(const Plan &p);
+hipError_t launch_mask_backward(const Plan &p, const BwdPlan &b, const void *x, const void *Wm,
+                                const Routing &r, const float *sg, float beta, float *dz,
+                                float *dW, float *dx, float *d_gate, void *ws, hipStream_t s);
 // routing statistics added to caller-owned 64-bit counters (NULL: skipped)
 hipError_t launch_stats(const Plan &p, const Routing &r, uint64_t *rank_masked,
                         uint64_t *active_hist, uint64_t *expert_load, hipStream_t s);

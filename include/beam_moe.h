@@ -138,6 +138,8 @@ typedef struct beam_moe_sizes {
     int32_t path;              /* 0 = streaming kernels; 1 = tiled kernels (or,
                                   without BEAM_FORCE_PREFILL, streaming ones
                                   when the device finds few pairs per expert) */
+    size_t  mask_backward_workspace_bytes; /* bytes needed by
+                                  beam_moe_mask_backward                        */
 } beam_moe_sizes;
 
 /* beam_moe_query: validate `desc` and fill `out`.
@@ -171,6 +173,33 @@ int beam_moe_forward_ex(const beam_moe_desc *desc, const void *x, const void *W_
                         void *y, const beam_moe_routing *out, void *ws,
                         size_t ws_bytes, hipStream_t stream,
                         hipEvent_t *stage_events);
+
+/* beam_moe_mask_backward: gradients of the mask router for one layer call
+ * (BEAM paper, section 3.3: straight-through estimation of the binarisation;
+ * news article on the paper, section 4: a beta-weighted sparsity term over
+ * the Top-K candidates' mask scores).  For token t, slot k (expert id_k,
+ * softmax weight g_k, hard mask m_k, mask logit z = z[t, id_k]) and
+ * slot_grad[t, k] = dL/dg_hat_k (the dot product of dL/dy_t with expert
+ * id_k's output; needed for masked slots too):
+ *   d_mask_logits[t, id_k] = (g_k * slot_grad[t,k] + beta) * sig(z)(1 - sig(z)),
+ *                            0 at non-candidates       [T, E], required
+ *   dW_mask = d_mask_logits^T x                       [E, d] or NULL
+ *   dx      = d_mask_logits W_mask (mask router only)  [T, d] or NULL
+ *   d_gate_logits[t, id_j] = g_j (m_j s_j - sum_k g_k m_k s_k), s = slot_grad,
+ *                            0 off the Top-K           [T, E] or NULL
+ * i.e. dL/dm_hat = dL/dm (STE) plus beta from L_sp = beta * sum over tokens
+ * and candidates of m_hat.  All outputs float32, overwritten (not added to).
+ * Reads routing->topk_ids, topk_weights, mask and mask_logits (of the
+ * forward of `desc`, earlier on the same stream).  bf16 layers form dW_mask
+ * on the matrix cores from d_mask_logits rounded to bf16 (float32
+ * accumulation); dx and the other outputs use float32 arithmetic.
+ * ws: at least sizes.mask_backward_workspace_bytes (may be 0 for float32
+ * layers).  Errors as for beam_moe_forward; beta must be finite. */
+int beam_moe_mask_backward(const beam_moe_desc *desc, const void *x, const void *W_mask,
+                           const beam_moe_routing *routing, const float *slot_grad, float beta,
+                           float *d_mask_logits, float *dW_mask, float *dx,
+                           float *d_gate_logits, void *ws, size_t ws_bytes,
+                           hipStream_t stream);
 
 /* beam_moe_stats: routing statistics, accumulated on the device.  They are
  * the quantities of the paper's analysis of the learned mask (news article on

@@ -27,11 +27,33 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, n), f"{n} declared in beam_moe.h but not exported"
 
 
-def test_header_struct_layout_matches_binding():
-    # the ctypes mirrors must have the sizes the C structs have on x86-64
-    assert ctypes.sizeof(B.Desc) == 4 * 9 + 4 * 3
-    assert ctypes.sizeof(B.Routing) == 13 * 8
-    assert ctypes.sizeof(B.Sizes) == 8 * 4 + 4 * 2
+def test_header_struct_layout_matches_binding(tmp_path):
+    # the ctypes mirrors must have the sizes and field offsets that a C
+    # compiler gives the header's structs
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    structs = {"beam_moe_desc": B.Desc, "beam_moe_routing": B.Routing, "beam_moe_sizes": B.Sizes}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "beam_moe.h"', 'int main(void) {']
+    for cname, py in structs.items():
+        lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'printf("{cname}.{f} %zu\\n", offsetof({cname}, {f}));')
+    lines.append("return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(__file__), "..", "include")
+    subprocess.run([cc, "-D__HIP_PLATFORM_AMD__", "-I", inc, "-I", "/opt/rocm/include", str(src),
+                    "-o", str(exe)], check=True)
+    got = dict(l.split() for l in subprocess.run([str(exe)], check=True, capture_output=True,
+                                                   text=True).stdout.splitlines())
+    for cname, py in structs.items():
+        assert int(got[cname]) == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert int(got[f"{cname}.{f}"]) == getattr(py, f).offset, f"{cname}.{f}"
 
 
 def test_version_and_strerror():
