@@ -21,7 +21,8 @@ plain Top-K), a sweep over the decode batch sizes, the prefill runs (keep
 0.15 / 0.3 / 0.5 / 1.0 at T = 2048 and 8192, and the skewed T = 16384 load),
 a stack of 48 distinct layers at T = 64 under the skewed load (eager and as
 one replayed HIP graph), a DeepSeekV2-Lite-shaped layer with two always-on
-shared experts (decode, masked and all-ones), the d=4096/I=1536 layer (decode T = 1 and 64,
+shared experts (decode, masked and all-ones), the mask-router backward
+(straight-through estimator + sparsity term), the d=4096/I=1536 layer (decode T = 1 and 64,
 prefill T = 4096, keep 0.15 and 0.5), and the fp64 oracle timed on this
 host's cores on a bounded sample of the headline workload.
 """
@@ -83,6 +84,9 @@ def parse():
     ap.add_argument("--no-stack", dest="stack", action="store_false")
     ap.add_argument("--stack-T", type=int, default=64)
     ap.add_argument("--stack-steps", type=int, default=20)
+    ap.add_argument("--backward", action="store_true", default=True,
+                    help="also time the mask-router backward at T = 256, 2048, 8192")
+    ap.add_argument("--no-backward", dest="backward", action="store_false")
     ap.add_argument("--shared", action="store_true", default=True,
                     help="also measure the DeepSeekV2-Lite-shaped layer with 2 shared experts")
     ap.add_argument("--no-shared", dest="shared", action="store_false")
@@ -429,6 +433,11 @@ def main():
     if args.shared and not args.only_headline:
         shared = run_shared(B, synth, dev, measure, args)
 
+    # ---- mask-router backward (STE + sparsity term) ------------------------
+    backward = None
+    if args.backward and not args.only_headline:
+        backward = run_backward(B, sets, shape, dev)
+
     prefill_out = [] if args.only_headline else run_prefill()
 
     # ---- CPU baseline: the fp64 oracle on this host's cores ---------------
@@ -479,6 +488,7 @@ def main():
         "prefill": prefill_out,
         "stack": stack,
         "shared": shared,
+        "mask_backward": backward,
         "large": large,
         "cpu_baseline": cpu,
     }
@@ -555,6 +565,49 @@ def run_stack(B, synth, sets, shape, dev, T, steps, dims):
            "bytes_per_step": byts, "eager": eager, "graph": graph}
     del g, Ls
     return out
+
+
+def run_backward(B, sets, shape, dev, steps=20):
+    """beam_moe_mask_backward after a forward of the headline layer, T = 256,
+    2048 and 8192 tokens (slot gradients drawn once per T).  Algorithmic
+    bytes: x read (T d bf16), dx and the two [T, E] float32 logit gradients
+    written, dW_mask written; FLOPs of the dW contraction 2 T E d."""
+    import torch
+
+    d, E, K = shape.d, shape.E, shape.K
+    out = []
+    for T in (256, 2048, 8192):
+        S = sets[0]
+        x = S["x"][:T].contiguous() if S["x"].shape[0] >= T else None
+        if x is None:
+            from dynamic_expert_sparsity_amd import synth
+            x = synth.make_tokens(shape, T, seed=0, layer=0, device=dev)
+        lay = B.MoELayer(S["W_gate"], S["W_mask"], S["W_gu"], S["W_dt"], K)
+        lay(x)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(T)
+        sg = torch.randn((T, K), generator=gen, device=dev, dtype=torch.float32)
+        for _ in range(3):
+            lay.mask_backward(x, sg, 0.01)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for a, b in evs:
+            a.record()
+            lay.mask_backward(x, sg, 0.01)
+            b.record()
+        torch.cuda.synchronize()
+        per = [a.elapsed_time(b) for a, b in evs]
+        ms = pct(per, 0.5)
+        byts = T * d * 2 + T * d * 4 + 2 * T * E * 4 + E * d * 4
+        flops = 2.0 * T * E * d
+        out.append({"T": T, "per_call": dist(per), "alg_bytes": byts,
+                    "GBps": round(byts / (ms * 1e-3) / 1e9, 1),
+                    "hbm_frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                    "dW_TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2)})
+        log(f"mask backward T={T}: {ms * 1e3:.1f} us")
+        del lay
+    return {"workload": f"d{d}-E{E}-K{K}-bf16 mask router backward, beta 0.01", "runs": out}
 
 
 def run_shared(B, synth, dev, measure, args):

@@ -101,7 +101,7 @@ int make_plan(const beam_moe_desc *desc, Plan &p) {
     p.off_tile_mask = off; off = align_up(off + (size_t)p.n_tiles * p.E2 * 8, 256);
     p.off_tile_base = off; off = align_up(off + (size_t)p.n_tiles * p.E2 * 4, 256);
     p.off_pair_pos = off;  off = align_up(off + (size_t)PT * 4, 256);
-    p.off_meta = off;      off = align_up(off + (size_t)(p.E2 + 1) * 16, 256);
+    p.off_meta = off;      off = align_up(off + 16, 256);
     // position blocks of <= 32: at most one partial block per active expert
     p.off_pbt = off;       off = align_up(off + (size_t)(p.max_active + PT / 32 + 1) * 16, 256);
     // sorted tokens, plus 32 slack entries read (not used) past a block end

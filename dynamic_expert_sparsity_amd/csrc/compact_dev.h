@@ -31,12 +31,10 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 // Wave 0 only (lane = threadIdx.x < 64): from per-expert counts s_cnt[E]
 // (E <= 256, four experts per lane) write block-padded exclusive offsets to
 // s_off[0..E] and r.expert_offsets, the ascending active-expert list and
-// r.num_active = {P, num_padded, n_active_experts, n_blocks}, and the E
-// records meta[i] = {expert, offset, count, 0} of the active experts in
-// ascending order followed by zero records, which the expert kernels start
-// from (count 0: nothing to do), the call's record meta[E] = {mode, max count,
-// position blocks, 0}, and one record {expert, first position, rows, 0} per
-// block of up to 32 consecutive positions of an expert (pbt, in expert order).
+// r.num_active = {P, num_padded, n_active_experts, n_blocks}, the call's
+// record meta = {mode, max count, position blocks, 0}, and one record
+// {expert, first position, rows, 0} per block of up to 32 consecutive
+// positions of an expert (pbt, in expert order).
 __device__ __forceinline__ void offsets_from_counts(const int *s_cnt, int *s_off, int E, int bm,
                                                     const Routing &r, int32_t *meta,
                                                     int32_t *pbt, int split, int lane) {
@@ -78,10 +76,7 @@ __device__ __forceinline__ void offsets_from_counts(const int *s_cnt, int *s_off
             s_off[ex] = op;
             r.expert_offsets[ex] = op;
             r.expert_counts[ex] = c[j];
-            if (act[j]) {
-                r.active_experts[oa] = ex;
-                *reinterpret_cast<int4 *>(meta + 4 * oa) = make_int4(ex, op, c[j], 0);
-            }
+            if (act[j]) r.active_experts[oa] = ex;
             if (mode == 0)
                 for (int q = 0; q < npb[j]; ++q)
                     *reinterpret_cast<int4 *>(pbt + 4 * (ob + q)) =
@@ -91,10 +86,6 @@ __device__ __forceinline__ void offsets_from_counts(const int *s_cnt, int *s_off
         oa += act[j];
         ob += npb[j];
     }
-    // slots past the active count get count 0, the expert kernels' exit test
-    const int n_act = __shfl(ia, 63);
-    for (int q = n_act + lane; q < E; q += 64)
-        *reinterpret_cast<int4 *>(meta + 4 * q) = make_int4(0, 0, 0, 0);
     if (lane == 63) {
         s_off[E] = ip;
         r.expert_offsets[E] = ip;
@@ -102,7 +93,7 @@ __device__ __forceinline__ void offsets_from_counts(const int *s_cnt, int *s_off
         r.num_active[1] = ip;
         r.num_active[2] = ia;
         r.num_active[3] = ip / bm;
-        *reinterpret_cast<int4 *>(meta + 4 * E) = make_int4(mode, mx, ib, 0);
+        *reinterpret_cast<int4 *>(meta) = make_int4(mode, mx, ib, 0);
     }
 }
 

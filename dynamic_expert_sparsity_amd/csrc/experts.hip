@@ -18,206 +18,6 @@
 namespace beam {
 
 // ---------------------------------------------------------------------------
-// Weight-streaming path (decode, bf16).
-//
-// The k-loop of a wave streams NK steps of 32 elements; every step is one
-// 16-byte load per lane per operand row (the MFMA 16x16x32 operand layout),
-// and the loads run PF steps ahead of the MFMAs in a ring of register slots.
-// With NK a compile-time constant the loop is fully unrolled, so the ring
-// needs no register copies and the wait counts stay exact; NK = 0 selects a
-// runtime-count loop for other sizes.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void stream_k2_rt(const bf16_t *__restrict__ b0,
-                                             const bf16_t *__restrict__ b1,
-                                             const bf16_t *__restrict__ a, int nk, f32x4 &acc0,
-                                             f32x4 &acc1) {
-    for (int k = 0; k < nk; ++k) {
-        const u32x4 av = ld16(a + 32 * k);
-        acc0 = mfma16x16x32(av, ld16(b0 + 32 * k), acc0);
-        acc1 = mfma16x16x32(av, ld16(b1 + 32 * k), acc1);
-    }
-}
-
-template <int NK, int PF>
-__device__ __forceinline__ void stream_k1_lds(const bf16_t *__restrict__ b,
-                                              const bf16_t *__restrict__ a_lds, f32x4 &acc) {
-    // acc += A * B over NK k-steps; A from LDS
-    u32x4 rb[PF];
-#pragma unroll
-    for (int p = 0; p < PF; ++p)
-        if (p < NK) rb[p] = ld16(b + 32 * p);
-#pragma unroll
-    for (int k = 0; k < NK; ++k) {
-        const int sl = k % PF;
-        const u32x4 w = rb[sl];
-        if (k + PF < NK) rb[sl] = ld16(b + 32 * (k + PF));
-        const u32x4 av = *reinterpret_cast<const u32x4 *>(a_lds + 32 * k);
-        acc = mfma16x16x32(av, w, acc);
-    }
-}
-
-__device__ __forceinline__ void stream_k1_lds_rt(const bf16_t *__restrict__ b,
-                                                 const bf16_t *__restrict__ a_lds, int nk,
-                                                 f32x4 &acc) {
-    for (int k = 0; k < nk; ++k)
-        acc = mfma16x16x32(*reinterpret_cast<const u32x4 *>(a_lds + 32 * k),
-                           ld16(b + 32 * k), acc);
-}
-
-// Up projection, streaming.  A unit is (active expert, 16 intermediate
-// units): 16 gate rows + 16 up rows of W_gu, streamed once.  The expert's
-// tokens (16 per MFMA row block; more are looped) form the A operand straight
-// from x; the NW waves split d (NK k-steps each) and their partial sums meet
-// in LDS.  Latency chain per unit: the expert's record {e, offset, count}
-// (scalar load) -> every weight fragment of the wave is requested at once ->
-// the block's 16 token ids (scalar loads, so they do not queue behind the
-// weights) -> the x fragments.  Scheduling barriers keep the compiler from
-// spreading the loads over the MFMAs; the weights stay in registers across
-// further 16-token blocks.  Grid: max_active * (I / 16); units past the
-// device-side active-expert count exit at once.
-template <int NW, int NK>
-__global__ __launch_bounds__(NW * 64) void up_stream_bf16(
-    const bf16_t *__restrict__ x, const bf16_t *__restrict__ Wgu,
-    const int32_t *__restrict__ meta, const int32_t *__restrict__ num_active,
-    const int32_t *__restrict__ sorted_tok, bf16_t *__restrict__ h, int d, int I,
-    const int32_t *__restrict__ mode) {
-    // mode: NULL, or the per-call choice (1: this call's experts take the tiled kernels)
-    if (mode != nullptr && *mode == 1) return;
-    const int ncg = I >> 4;
-    const int ai = blockIdx.x / ncg;
-    const int cg = blockIdx.x - ai * ncg;
-    // ai < max_active <= E: the record exists; count 0 marks an inactive slot
-    const i32x4 mt = sload16(meta + 4 * ai);
-    if (mt[2] == 0) return;
-    const int e = mt[0], off = mt[1], cnt = mt[2];
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int li = lane & 15;
-    const int kq = (lane >> 4) * 8;
-    const int dq = d / NW;
-    const int kb = wave * dq;
-    const bf16_t *bg = Wgu + ((size_t)e * 2 * I + cg * 16 + li) * d + kb + kq;
-    const bf16_t *bu = bg + (size_t)I * d;
-    __shared__ f32x4 red[NW][2][64];
-
-    u32x4 rg[NK > 0 ? NK : 1], ru[NK > 0 ? NK : 1], rx[NK > 0 ? NK : 1];
-    if constexpr (NK > 0) {
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int k = 0; k < NK; ++k) {
-            rg[k] = ld16(bg + 32 * k);
-            ru[k] = ld16(bu + 32 * k);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    for (int pc = 0; pc < cnt; pc += 16) {
-        // token ids of the block's 16 positions (inside the padded segment)
-        const int *st = sorted_tok + off + pc;
-        int tok = st[0];
-#pragma unroll
-        for (int j = 1; j < 16; ++j) {
-            const int v = st[j];
-            tok = li == j ? v : tok;
-        }
-        // positions past the count: zero operands, no load (a decode expert
-        // has a few tokens, so most of the 16 rows are such pads)
-        const bool have = pc + li < cnt;
-        tok = have ? tok : 0;
-        const bf16_t *xa = x + (size_t)tok * d + kb + kq;
-        f32x4 ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (NK > 0) {
-            __builtin_amdgcn_sched_barrier(0);
-            if (have) {
-#pragma unroll
-                for (int k = 0; k < NK; ++k) rx[k] = ld16(xa + 32 * k);
-            } else {
-#pragma unroll
-                for (int k = 0; k < NK; ++k) rx[k] = u32x4{0u, 0u, 0u, 0u};
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int k = 0; k < NK; ++k) {
-                ag = mfma16x16x32(rx[k], rg[k], ag);
-                au = mfma16x16x32(rx[k], ru[k], au);
-            }
-        } else {
-            stream_k2_rt(bg, bu, xa, dq >> 5, ag, au);
-        }
-        red[wave][0][lane] = ag;
-        red[wave][1][lane] = au;
-        __syncthreads();
-        if (wave == 0) {
-            f32x4 sg = red[0][0][lane], su = red[0][1][lane];
-#pragma unroll
-            for (int w = 1; w < NW; ++w) {
-                sg += red[w][0][lane];
-                su += red[w][1][lane];
-            }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int row = pc + (lane >> 4) * 4 + q;
-                if (row < cnt)
-                    h[(size_t)(off + row) * I + cg * 16 + li] =
-                        f32_to_bf16(silu<false>(sg[q]) * su[q]);
-            }
-        }
-        __syncthreads();
-    }
-}
-
-// Down projection, streaming: a unit is (active expert, 64 output channels);
-// each wave owns 16 channels (16 rows of W_dt[e], each I long) over all of I
-// (NK = I / 32 k-steps).  The 16 h rows of the current position block are
-// staged in LDS once per workgroup (row pitch I + 8 elements keeps the MFMA
-// reads conflict-free).
-template <int NK>
-__global__ __launch_bounds__(256) void down_stream_bf16(
-    const bf16_t *__restrict__ Wdt, const bf16_t *__restrict__ h,
-    const int32_t *__restrict__ meta, const int32_t *__restrict__ num_active,
-    bf16_t *__restrict__ o, int d, int I, const int32_t *__restrict__ mode) {
-    if (mode != nullptr && *mode == 1) return;
-    extern __shared__ __align__(16) unsigned char lds_raw[];
-    bf16_t *hs = reinterpret_cast<bf16_t *>(lds_raw);
-    const int pitch = I + 8;
-    const int ncg = d >> 6;
-    const int ai = blockIdx.x / ncg;
-    const int cg = blockIdx.x - ai * ncg;
-    // ai < max_active <= E: the record exists; count 0 marks an inactive slot
-    const i32x4 mt = sload16(meta + 4 * ai);
-    if (mt[2] == 0) return;
-    const int e = mt[0], off = mt[1], cnt = mt[2];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int kq = (lane >> 4) * 8;
-    const int c = cg * 64 + wave * 16 + (lane & 15);
-    const bf16_t *brow = Wdt + ((size_t)e * d + c) * I + kq;
-    const bf16_t *arow = hs + (lane & 15) * pitch + kq;
-    const int chunks = I >> 3;  // 16-byte chunks per row
-
-    for (int pc = 0; pc < cnt; pc += 16) {
-        // rows past the count are zero-filled, not loaded (a decode expert
-        // has a few tokens); their results land in D rows that are not stored
-        const int nrow = min(16, cnt - pc);
-        for (int q = tid; q < 16 * chunks; q += 256) {
-            const int row = q / chunks, ch = q - row * chunks;
-            *reinterpret_cast<u32x4 *>(hs + row * pitch + ch * 8) =
-                row < nrow ? ld16(h + (size_t)(off + pc + row) * I + ch * 8) : u32x4{0u, 0u, 0u, 0u};
-        }
-        __syncthreads();
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (NK > 0) stream_k1_lds<NK, (NK < 8 ? NK : 8)>(brow, arow, acc);
-        else stream_k1_lds_rt(brow, arow, I >> 5, acc);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int row = pc + (lane >> 4) * 4 + q;
-            if (row < cnt) o[(size_t)(off + row) * d + c] = f32_to_bf16(acc[q]);
-        }
-        __syncthreads();
-    }
-}
-
-// ---------------------------------------------------------------------------
 // Generic path (float32 layer): one workgroup per block of bm sorted
 // positions, one thread per output column; plain fp32 FMAs.
 // ---------------------------------------------------------------------------
@@ -333,7 +133,7 @@ __global__ __launch_bounds__(256) void combine_bf16(const bf16_t *__restrict__ o
 }
 
 // ---------------------------------------------------------------------------
-// Up and down projections, ring-streamed (bf16, k length % 256 == 0).  A
+// Up and down projections, ring-streamed (bf16, k length % 64 == 0).  A
 // unit is (block of up to 32 positions of one expert, column group): 32 rows
 // of the expert's weights (up: 16 gate + 16 up rows; down: 32 output
 // channels).  A persistent grid of one 8-wave workgroup per CU walks a
@@ -347,7 +147,10 @@ __global__ __launch_bounds__(256) void combine_bf16(const bf16_t *__restrict__ o
 // LDS and the compiler tracks no in-flight register loads.  Waits are
 // explicit vmcnt counts per wave: a chunk is 2 weight loads and 1 or 2 x
 // loads; the h stores that end a unit are not counted, which only makes the
-// next waits stricter.
+// next waits stricter.  A k length that is not a multiple of 256 ends in a
+// short chunk: its loads past the row end are pointed at the chunk's start
+// (in bounds, never used) and the waves whose k-slice lies past the end skip
+// their MFMAs for it.
 // ---------------------------------------------------------------------------
 constexpr int RING_NS = 4;                         // LDS slots
 constexpr int RING_W = 32 * 512;                   // weight rows of a slot
@@ -384,8 +187,8 @@ __device__ __forceinline__ void ring_dma(const void *g, unsigned char *l) {
 // gate and 16 up rows of a column group of 16 units; out h = SiLU(a) * u).
 // DOWN = true: down projection (A = the block's h rows, B = 32 rows of W_dt,
 // one per output channel of a column group of 32; out o).  klen = d (up) or
-// I (down), a multiple of 256; ncols = I (up) or d (down).
-template <bool DOWN>
+// I (down), a multiple of 64; ncols = I (up) or d (down).
+template <bool DOWN, bool TAIL>
 __global__ __launch_bounds__(512, 1) void ring_bf16(
     const bf16_t *__restrict__ A, const bf16_t *__restrict__ W,
     const int32_t *__restrict__ pbt, const int32_t *__restrict__ mrec,
@@ -396,7 +199,9 @@ __global__ __launch_bounds__(512, 1) void ring_bf16(
     f32x4 *red = reinterpret_cast<f32x4 *>(lds + NS * RING_SLOT);  // [wave][2 col blocks x 2 row blocks][lane]
     // mrec = {mode, max count, position blocks, 0}; mode 1: the tiled kernels take this call
     if (check_mode && mrec[0] == 1) return;
-    const int NCH = klen >> 8;                     // k-chunks of 256 per row
+    const int NCH = (klen + 255) >> 8;             // k-chunks of 256 per row (last may be short)
+    // elements of a short last chunk (TAIL instances only; else klen % 256 == 0)
+    const int tail = TAIL ? (klen & 255) : 0;
     const int ncg = DOWN ? ncols >> 5 : ncols >> 4;  // column groups per position block
     const int NU = mrec[2] * ncg;
     const int G = gridDim.x, b = blockIdx.x;
@@ -421,6 +226,7 @@ __global__ __launch_bounds__(512, 1) void ring_bf16(
     // weight loads: instruction i covers rows 4 wave + 2 i + {0, 1}; lane l
     // fetches piece (l % 32) ^ (r % 16) of row r = 4 wave + 2 i + l / 32
     const int wr0 = 4 * wave + (lane >> 5), wr1 = wr0 + 2;
+    const int wp0 = (lane & 31) ^ (wr0 & 15), wp1 = (lane & 31) ^ (wr1 & 15);  // weight pieces
     // A loads: lane l -> position 16 blk + l / 4, piece (l % 4) ^ ((l / 16) % 4)
     const int xp = lane >> 2;
     const int xpiece = (lane & 3) ^ ((lane >> 4) & 3);
@@ -439,8 +245,8 @@ __global__ __launch_bounds__(512, 1) void ring_bf16(
             const int e = rec.x, pos0 = rec.y, rows = rec.z;
             const size_t wrows = DOWN ? (size_t)ncols : (size_t)2 * ncols;  // rows of W[e]
             const bf16_t *we = W + (size_t)e * wrows * klen;
-            wrow0 = we + (size_t)wmap(wr0, cg) * klen + (((lane & 31) ^ (wr0 & 15)) << 3);
-            wrow1 = we + (size_t)wmap(wr1, cg) * klen + (((lane & 31) ^ (wr1 & 15)) << 3);
+            wrow0 = we + (size_t)wmap(wr0, cg) * klen + (wp0 << 3);
+            wrow1 = we + (size_t)wmap(wr1, cg) * klen + (wp1 << 3);
             int a0, a1;  // A rows of this lane's positions xp and 16 + xp
             if (DOWN) {
                 a0 = pos0 + (xp < rows ? xp : 0);
@@ -470,12 +276,17 @@ __global__ __launch_bounds__(512, 1) void ring_bf16(
             scg[q] = i_cg;
         }
         unsigned char *sl = lds + q * RING_SLOT;
-        ring_dma<2>(wrow0 + c * 256, sl + (4 * wave) * 512);
-        ring_dma<2>(wrow1 + c * 256, sl + (4 * wave + 2) * 512);
+        // a short last chunk: pieces past the row end load the chunk's start instead
+        const bool shrt = TAIL && tail != 0 && c == NCH - 1;
+        const int w0o = shrt && (wp0 << 3) >= tail ? -(wp0 << 3) : 0;
+        const int w1o = shrt && (wp1 << 3) >= tail ? -(wp1 << 3) : 0;
+        const int xo = shrt && wave * 32 >= tail ? -(wave * 32 + xpiece * 8) : 0;
+        ring_dma<2>(wrow0 + c * 256 + w0o, sl + (4 * wave) * 512);
+        ring_dma<2>(wrow1 + c * 256 + w1o, sl + (4 * wave + 2) * 512);
         unsigned char *xs = sl + RING_W + wave * 2048;
-        ring_dma<0>(xa0 + c * 256, xs);
+        ring_dma<0>(xa0 + c * 256 + xo, xs);
         if (i_rows > 16) {
-            ring_dma<0>(xa1 + c * 256, xs + 1024);
+            ring_dma<0>(xa1 + c * 256 + xo, xs + 1024);
             ld[q] = 4;
         } else {
             ld[q] = 3;
@@ -509,15 +320,19 @@ __global__ __launch_bounds__(512, 1) void ring_bf16(
             const u32x4 w1 = *reinterpret_cast<const u32x4 *>(sl + (16 + li) * 512 + ((gc ^ li) << 4));
             const unsigned char *xs = sl + RING_W + wave * 2048;
             const int xo = li * 64 + ((kg ^ ((li >> 2) & 3)) << 4);
-            const u32x4 a0 = *reinterpret_cast<const u32x4 *>(xs + xo);
-            c00 = mfma16x16x32(a0, w0, c00);
-            c10 = mfma16x16x32(a0, w1, c10);
-            if (rb1) {
-                const u32x4 a1 = *reinterpret_cast<const u32x4 *>(xs + 1024 + xo);
-                c01 = mfma16x16x32(a1, w0, c01);
-                c11 = mfma16x16x32(a1, w1, c11);
-            }
             const int uu = j / NCH;
+            // this wave's k-slice lies past the end of a short last chunk
+            const bool idle = TAIL && tail != 0 && j - uu * NCH == NCH - 1 && wave * 32 >= tail;
+            if (!idle) {
+                const u32x4 a0 = *reinterpret_cast<const u32x4 *>(xs + xo);
+                c00 = mfma16x16x32(a0, w0, c00);
+                c10 = mfma16x16x32(a0, w1, c10);
+                if (rb1) {
+                    const u32x4 a1 = *reinterpret_cast<const u32x4 *>(xs + 1024 + xo);
+                    c01 = mfma16x16x32(a1, w0, c01);
+                    c11 = mfma16x16x32(a1, w1, c11);
+                }
+            }
             if (j - uu * NCH == NCH - 1) {
                 // unit done: the eight waves' partial sums meet in LDS
                 red[(wave * 4 + 0) * 64 + lane] = c00;
@@ -561,10 +376,9 @@ __global__ __launch_bounds__(512, 1) void ring_bf16(
     }
 }
 
-// the ring kernels: bf16 and a k length (d for up, I for down) that is a
-// multiple of 256 (I % 16 == 0 and d % 32 == 0 then hold for the column groups)
-static bool ring_ok_up(const Plan &p) { return p.dtype == 1 && p.d % 256 == 0 && p.I % 16 == 0; }
-static bool ring_ok_down(const Plan &p) { return p.dtype == 1 && p.I % 256 == 0 && p.d % 32 == 0; }
+// The ring kernels need a k length (d for up, I for down) that is a multiple
+// of 64 and whole column groups (I % 16 for up, d % 32 for down): the
+// descriptor checks of a bf16 layer (d % 128 == 0, I % 64 == 0) imply both.
 static int ring_grid() {
     static int n = 0;
     static std::once_flag once;
@@ -591,6 +405,18 @@ static hipError_t ring_attr(const void *fn) {
     return hipSuccess;
 }
 
+// one ring launch; TAIL: the k length ends in a short chunk
+template <bool DOWN, bool TAIL>
+static hipError_t launch_ring(const void *A, const void *W, const Plan &p, const Work &w, void *out,
+                              int klen, int ncols, hipStream_t s) {
+    const hipError_t e = ring_attr((const void *)ring_bf16<DOWN, TAIL>);
+    if (e != hipSuccess) return e;
+    ring_bf16<DOWN, TAIL><<<ring_grid(), 512, RING_LDS, s>>>(
+        (const bf16_t *)A, (const bf16_t *)W, w.pbt, w.meta, w.sorted_tok,
+        (bf16_t *)out, klen, ncols, p.path == 1 ? 1 : 0);
+    return hipGetLastError();
+}
+
 hipError_t launch_expert_up(const Plan &p, const void *x, const void *W_gu, const Routing &r,
                             const Work &w, hipStream_t s) {
     if (p.path == 1) {
@@ -599,32 +425,10 @@ hipError_t launch_expert_up(const Plan &p, const void *x, const void *W_gu, cons
         const hipError_t e = launch_gemm_up(p, x, W_gu, r, w, s);
         if (e != hipSuccess || p.split == 0) return e;
     }
-    if (ring_ok_up(p)) {
-        const hipError_t e = ring_attr((const void *)ring_bf16<false>);
+    if (p.dtype == 1) {
+        const hipError_t e = p.d % 256 == 0 ? launch_ring<false, false>(x, W_gu, p, w, w.h, p.d, p.I, s)
+                                            : launch_ring<false, true>(x, W_gu, p, w, w.h, p.d, p.I, s);
         if (e != hipSuccess) return e;
-        ring_bf16<false><<<ring_grid(), 512, RING_LDS, s>>>(
-            (const bf16_t *)x, (const bf16_t *)W_gu, w.pbt, w.meta + 4 * p.E2, w.sorted_tok,
-            (bf16_t *)w.h, p.d, p.I, p.path == 1 ? 1 : 0);
-    } else if (p.dtype == 1) {
-        const unsigned grid = (unsigned)p.max_active * (unsigned)(p.I / 16);
-#define BEAM_UP(NWV, NKV)                                                                     \
-    up_stream_bf16<NWV, NKV><<<grid, NWV * 64, 0, s>>>(                                      \
-        (const bf16_t *)x, (const bf16_t *)W_gu, w.meta, r.num_active, w.sorted_tok,          \
-        (bf16_t *)w.h, p.d, p.I, p.path == 1 ? w.meta + 4 * p.E2 : nullptr)
-        if (p.d % 256 == 0) {  // eight waves split d, d / 256 k-steps each
-            switch (p.d / 256) {
-                case 1: BEAM_UP(8, 1); break;
-                case 2: BEAM_UP(8, 2); break;
-                case 4: BEAM_UP(8, 4); break;
-                case 8: BEAM_UP(8, 8); break;
-                case 12: BEAM_UP(8, 12); break;
-                case 16: BEAM_UP(8, 16); break;
-                default: BEAM_UP(8, 0); break;
-            }
-        } else {               // four waves, d / 128 k-steps each
-            BEAM_UP(4, 0);
-        }
-#undef BEAM_UP
     } else {
         const dim3 grid((unsigned)p.n_blocks_cap, (p.I + 255) / 256);
         up_generic<float><<<grid, 256, 0, s>>>((const float *)x, (const float *)W_gu,
@@ -640,31 +444,10 @@ hipError_t launch_expert_down(const Plan &p, const void *W_dt, const Routing &r,
         const hipError_t e = launch_gemm_down(p, W_dt, r, w, s);
         if (e != hipSuccess || p.split == 0) return e;
     }
-    if (ring_ok_down(p)) {
-        const hipError_t e = ring_attr((const void *)ring_bf16<true>);
+    if (p.dtype == 1) {
+        const hipError_t e = p.I % 256 == 0 ? launch_ring<true, false>(w.h, W_dt, p, w, w.o, p.I, p.d, s)
+                                            : launch_ring<true, true>(w.h, W_dt, p, w, w.o, p.I, p.d, s);
         if (e != hipSuccess) return e;
-        ring_bf16<true><<<ring_grid(), 512, RING_LDS, s>>>(
-            (const bf16_t *)w.h, (const bf16_t *)W_dt, w.pbt, w.meta + 4 * p.E2, w.sorted_tok,
-            (bf16_t *)w.o, p.I, p.d, p.path == 1 ? 1 : 0);
-    } else if (p.dtype == 1) {
-        const unsigned grid = (unsigned)p.max_active * (unsigned)(p.d / 64);
-        const size_t lds = (size_t)16 * (p.I + 8) * sizeof(bf16_t);
-#define BEAM_DOWN(NKV)                                                                        \
-    down_stream_bf16<NKV><<<grid, 256, lds, s>>>((const bf16_t *)W_dt, (const bf16_t *)w.h,   \
-                                                 w.meta, r.num_active, (bf16_t *)w.o, p.d,    \
-                                                 p.I, p.path == 1 ? w.meta + 4 * p.E2 : nullptr)
-        switch (p.I / 32) {  // k-steps per wave
-            case 2: BEAM_DOWN(2); break;
-            case 4: BEAM_DOWN(4); break;
-            case 8: BEAM_DOWN(8); break;
-            case 12: BEAM_DOWN(12); break;
-            case 16: BEAM_DOWN(16); break;
-            case 24: BEAM_DOWN(24); break;
-            case 32: BEAM_DOWN(32); break;
-            case 48: BEAM_DOWN(48); break;
-            default: BEAM_DOWN(0); break;
-        }
-#undef BEAM_DOWN
     } else {
         const dim3 grid((unsigned)p.n_blocks_cap, (p.d + 255) / 256);
         down_generic<float><<<grid, 256, 0, s>>>((const float *)W_dt, (const float *)w.h,

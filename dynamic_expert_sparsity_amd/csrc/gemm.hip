@@ -395,7 +395,7 @@ static GemmArgs base_args(const Plan &p, const Routing &r, const Work &w) {
     a.sorted_tok = w.sorted_tok;
     a.expert_offsets = r.expert_offsets;
     a.expert_counts = r.expert_counts;
-    a.mode = p.split == 0 ? nullptr : w.meta + 4 * p.E2;
+    a.mode = p.split == 0 ? nullptr : w.meta;
     a.T = p.T;
     a.d = p.d;
     a.I = p.I;

@@ -20,7 +20,7 @@ struct Plan {
                         // else (1) chosen per call on the device: tiled if the
                         // blocks of <= 32 positions number >= 1.5 x the active
                         // experts or one expert has more than 512 pairs (the
-                        // mode record after meta)
+                        // per-call record meta)
     float thr;          // mask logit threshold: m = [z >= thr]
     // select / compaction
     int s_ts;           // tokens per select tile (64)
@@ -49,8 +49,8 @@ struct Work {  // workspace views
     uint64_t *tile_mask;
     int32_t *tile_base;
     int32_t *pair_pos;   // [T*K] sorted position of each pair, -1 if masked
-    int32_t *meta;       // [E][4] per active expert: {expert, offset, count, 0},
-                         // then {mode (1 tiled, 0 streaming), max count, position blocks, 0}
+    int32_t *meta;       // [4] the call's record {mode (1 tiled, 0 streaming),
+                         // max count, position blocks, 0}
     int32_t *pbt;        // [pb_cap][4] per block of <= 32 positions of an expert:
                          // {expert, first position, rows, 0}
     int32_t *sorted_tok; // [cap] token of each sorted position (pads: unset)

@@ -59,6 +59,14 @@ def test_expert_counts_and_topk(E, K):
     _full_check(L, K)
 
 
+# streaming kernels whose k length ends in a short chunk (d % 256, I % 256 != 0)
+@pytest.mark.parametrize("d,I,T", [(384, 192, 70), (640, 320, 33), (128, 1408, 40)])
+def test_short_last_chunk(d, I, T):
+    shape = synth.LayerShape(d, 16, 4, I, torch.bfloat16)
+    L = layer(shape, T, seed=450 + d + I, mask_bias=0.0)
+    _full_check(L, 4)
+
+
 @pytest.mark.parametrize("bm", [16, 32, 64, 128])
 def test_block_sizes(bm):
     L = layer(SMALL, 200, seed=400 + bm, mask_bias=0.2)
