@@ -18,30 +18,37 @@ namespace beam {
 // ---------------------------------------------------------------------------
 // Router logits block, bf16, MFMA 16x16x32.  The two routers are one GEMM
 // with 2E output columns: column n < E is W_gate row n, column E + n is
-// W_mask row n.  A workgroup owns 16 columns and 16*MT tokens; its NW waves
-// split d (every wave requests all of its x and weight fragments before the
-// first MFMA) and their partial sums meet in LDS, where wave 0 adds them in
-// wave order and writes the finished float32 logits.  A (x rows) and B
-// (weight rows) are both k-contiguous, so every lane's 16-byte load lands
-// directly in MFMA layout.  Out-of-range tokens / columns load a clamped row
-// and their results are not stored.
+// W_mask row n.  A workgroup owns 16*NC columns and 16*MT tokens; its NW
+// waves split d (every wave requests a batch of its x and weight fragments
+// before the MFMAs that use them) and their partial sums meet in LDS, where
+// wave c adds them for column block c in wave order and writes the finished
+// float32 logits.  A (x rows) and B (weight rows) are both k-contiguous, so
+// every lane's 16-byte load lands directly in MFMA layout.  More column
+// blocks per workgroup read each x row fewer times (2E / (16 NC) times in
+// all); one block gives the most workgroups for small batches.  Out-of-range
+// tokens / columns load a clamped row and their results are not stored.
 // ---------------------------------------------------------------------------
-template <int MT, int NW>
+template <int MT, int NW, int NC>
 __global__ __launch_bounds__(NW * 64) void router_logits_bf16(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ Wg, const bf16_t *__restrict__ Wm,
     float *__restrict__ gate_logits, float *__restrict__ mask_logits, int T, int d, int E) {
-    __shared__ f32x4 red[NW][MT][64];
+    static_assert(NC <= NW, "one wave per column block in the final sum");
+    __shared__ f32x4 red[NW][MT][NC][64];
     const int rtile = blockIdx.x;
     const int cgroup = blockIdx.y;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int twoE = 2 * E;
-    const int n = cgroup * 16 + (lane & 15);
-    const int nc = n < twoE ? n : twoE - 1;
     const int kq = (lane >> 4) * 8;
     const int dq = d / NW;
     const int kb = wave * dq + kq;
-    const bf16_t *brow = (nc < E ? Wg + (size_t)nc * d : Wm + (size_t)(nc - E) * d) + kb;
+    const bf16_t *brow[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int n = (cgroup * NC + c) * 16 + (lane & 15);
+        const int nc = n < twoE ? n : twoE - 1;
+        brow[c] = (nc < E ? Wg + (size_t)nc * d : Wm + (size_t)(nc - E) * d) + kb;
+    }
     const int tbase = rtile * 16 * MT;
 
     const bf16_t *arow[MT];
@@ -51,41 +58,51 @@ __global__ __launch_bounds__(NW * 64) void router_logits_bf16(
         t = t < T ? t : T - 1;
         arow[m] = x + (size_t)t * d + kb;
     }
-    f32x4 acc[MT];
+    f32x4 acc[MT][NC];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) acc[m][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    constexpr int CH = 8;  // k-steps requested per batch
+    constexpr int CH = NC == 1 ? 8 : 4;  // k-steps requested per batch
     for (int k0 = 0; k0 < dq; k0 += 32 * CH) {
-        u32x4 b[CH], a[CH][MT];
+        u32x4 b[CH][NC], a[CH][MT];
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            const int k = k0 + 32 * c;
+        for (int j = 0; j < CH; ++j) {
+            const int k = k0 + 32 * j;
             if (k < dq) {
-                b[c] = ld16(brow + k);
 #pragma unroll
-                for (int m = 0; m < MT; ++m) a[c][m] = ld16(arow[m] + k);
+                for (int c = 0; c < NC; ++c) b[j][c] = ld16(brow[c] + k);
+#pragma unroll
+                for (int m = 0; m < MT; ++m) a[j][m] = ld16(arow[m] + k);
             }
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int c = 0; c < CH; ++c)
-            if (k0 + 32 * c < dq)
+        for (int j = 0; j < CH; ++j)
+            if (k0 + 32 * j < dq)
 #pragma unroll
-                for (int m = 0; m < MT; ++m) acc[m] = mfma16x16x32(a[c][m], b[c], acc[m]);
+                for (int m = 0; m < MT; ++m)
+#pragma unroll
+                    for (int c = 0; c < NC; ++c) acc[m][c] = mfma16x16x32(a[j][m], b[j][c], acc[m][c]);
     }
 
 #pragma unroll
-    for (int m = 0; m < MT; ++m) red[wave][m][lane] = acc[m];
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) red[wave][m][c][lane] = acc[m][c];
     __syncthreads();
-    if (wave != 0 || n >= twoE) return;
+    if (wave >= NC) return;
+    const int c = wave;  // this wave's column block
+    const int n = (cgroup * NC + c) * 16 + (lane & 15);
+    if (n >= twoE) return;
     float *out = n < E ? gate_logits + n : mask_logits + (n - E);
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-        f32x4 v = red[0][m][lane];
+        f32x4 v = red[0][m][c][lane];
 #pragma unroll
-        for (int w = 1; w < NW; ++w) v += red[w][m][lane];
+        for (int w = 1; w < NW; ++w) v += red[w][m][c][lane];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = tbase + m * 16 + (lane >> 4) * 4 + i;
@@ -386,25 +403,38 @@ static void launch_select_l(const Plan &p, const Routing &r, const Work &w, hipS
     }
 }
 
+#ifndef BEAM_ROUTER_GEMM_T
+#define BEAM_ROUTER_GEMM_T 2048
+#endif
+#ifndef BEAM_ROUTER_WIDE_T
+#define BEAM_ROUTER_WIDE_T 1024
+#endif
+
 hipError_t launch_route(const Plan &p, const void *x, const void *Wg, const void *Wm,
                         const Routing &r, const Work &w, hipStream_t s) {
-    if (p.dtype == 1 && p.path == 1 && p.T > 2048) {
-        // large batch: the logits as one dense MFMA GEMM (below ~2048 tokens its
-        // T / 128 tiles leave most CUs idle and the streaming kernel is faster)
+    if (p.dtype == 1 && p.path == 1 && p.T > BEAM_ROUTER_GEMM_T) {
+        // large batch: the logits as one dense MFMA GEMM
         hipError_t err = launch_gemm_router(p, x, Wg, Wm, r, s);
         if (err != hipSuccess) return err;
     } else if (p.dtype == 1) {
-        // few tokens: 16-token router tiles; more: 32-token tiles
-        const int mt = p.T <= 16 ? 1 : 2;
-        const dim3 grid((p.T + 16 * mt - 1) / (16 * mt), (2 * p.E + 15) / 16);
-#define BEAM_ROUTER(MTV, NWV)                                                                  \
-    router_logits_bf16<MTV, NWV><<<grid, NWV * 64, 0, s>>>(                                  \
+        // few tokens: 16-token tiles of one column block (the most
+        // workgroups); more: 32-token tiles; large batches: 64-token tiles of
+        // four column blocks, so x and the weights are each re-read fewer times
+        const int mt = p.T <= 16 ? 1 : p.T <= BEAM_ROUTER_WIDE_T ? 2 : 4;
+        const int ncb = p.T <= BEAM_ROUTER_WIDE_T ? 1 : 4;
+        const dim3 grid((p.T + 16 * mt - 1) / (16 * mt), (2 * p.E + 16 * ncb - 1) / (16 * ncb));
+#define BEAM_ROUTER(MTV, NWV, NCV)                                                             \
+    router_logits_bf16<MTV, NWV, NCV><<<grid, NWV * 64, 0, s>>>(                              \
         (const bf16_t *)x, (const bf16_t *)Wg, (const bf16_t *)Wm, r.gate_logits,            \
         r.mask_logits, p.T, p.d, p.E)
         if (p.d % 256 == 0) {
-            if (mt == 1) BEAM_ROUTER(1, 8); else BEAM_ROUTER(2, 8);
+            if (mt == 1) BEAM_ROUTER(1, 8, 1);
+            else if (mt == 2) BEAM_ROUTER(2, 8, 1);
+            else BEAM_ROUTER(4, 8, 4);
         } else {
-            if (mt == 1) BEAM_ROUTER(1, 4); else BEAM_ROUTER(2, 4);
+            if (mt == 1) BEAM_ROUTER(1, 4, 1);
+            else if (mt == 2) BEAM_ROUTER(2, 4, 1);
+            else BEAM_ROUTER(4, 4, 4);
         }
 #undef BEAM_ROUTER
     } else {
