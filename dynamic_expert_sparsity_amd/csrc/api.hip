@@ -61,12 +61,12 @@ int make_plan(const beam_moe_desc *desc, Plan &p) {
     if (D.dtype == BEAM_BF16 && (D.d % 128 != 0 || D.I % 64 != 0 || D.I > 2040))
         return fail(BEAM_EUNSUPPORTED,
                     "bf16 layer needs d %% 128 == 0, I %% 64 == 0 and I <= 2040 (d=%d I=%d)", D.d, D.I);
-    // the tiled (prefill) path: bf16, 256-position blocks, d % 256, I % 128
+    // the tiled (prefill) path: bf16, 128-position blocks, d % 256, I % 128
     const bool gemm_ok = D.dtype == BEAM_BF16 && D.d % 256 == 0 && D.I % 128 == 0 &&
-                         (D.block_m == 0 || D.block_m == 256);
+                         (D.block_m == 0 || D.block_m == 128);
     if ((D.flags & BEAM_FORCE_PREFILL) && !gemm_ok)
         return fail(BEAM_EUNSUPPORTED,
-                    "the tiled path needs bf16, d %% 256 == 0, I %% 128 == 0, block_m 0 or 256");
+                    "the tiled path needs bf16, d %% 256 == 0, I %% 128 == 0, block_m 0 or 128");
     const long long TK = (long long)D.T * D.K;
     const long long PT = (long long)D.T * (D.K + D.n_shared);
     if (PT > (1ll << 30)) return fail(BEAM_EUNSUPPORTED, "T*(K+n_shared)=%lld too large", PT);
@@ -79,7 +79,7 @@ int make_plan(const beam_moe_desc *desc, Plan &p) {
                      (!(D.flags & BEAM_FORCE_DECODE) && gemm_ok && D.T > 512)
                  ? 1
                  : 0;
-    p.bm = p.path == 1 ? 256 : (D.block_m ? D.block_m : 16);
+    p.bm = p.path == 1 ? 128 : (D.block_m ? D.block_m : 16);
     // with few active pairs per expert the weights stream faster through the
     // streaming kernels than through mostly empty 256-row GEMM tiles; the
     // device decides per call from the routed counts

@@ -197,8 +197,8 @@ __global__ __launch_bounds__(512, 1) void ring_bf16(
     constexpr int NS = RING_NS;
     extern __shared__ __align__(16) unsigned char lds[];
     f32x4 *red = reinterpret_cast<f32x4 *>(lds + NS * RING_SLOT);  // [wave][2 col blocks x 2 row blocks][lane]
-    // mrec = {mode, max count, position blocks, 0}; mode 1: the tiled kernels take this call
-    if (check_mode && mrec[0] == 1) return;
+    // mrec = {kernel family, max count, records, 0}; family 1 or 2: the tiled kernels take this call
+    if (check_mode && mrec[0] != 0) return;
     const int NCH = (klen + 255) >> 8;             // k-chunks of 256 per row (last may be short)
     // elements of a short last chunk (TAIL instances only; else klen % 256 == 0)
     const int tail = TAIL ? (klen & 255) : 0;

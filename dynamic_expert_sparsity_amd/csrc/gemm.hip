@@ -5,11 +5,15 @@
 // The same kernel, in ROUTER mode, computes the two routers' logits (Eq. 4-5)
 // of a large batch as one dense GEMM with 2E = 256 columns.
 //
-// Tile: BM rows (UP/DOWN: one 256-position block of one expert; ROUTER: 128
-// tokens) x 256 output columns, k in stages of 64.  BM / 32 waves, (BM / 64)
-// (rows) x 2 (columns), each 64 x 128 (2 x 4 MFMA tiles of 32 x 32), two
-// waves per SIMD; a wave whose 64 rows are all padding of its expert's last
-// block (or past the last token) skips its LDS reads and MFMAs.  UP: the 256
+// Tile: BM rows (UP/DOWN: one 128-position block of one expert, or 256
+// positions = up to two such blocks of one expert; ROUTER: 128 tokens) x 256
+// output columns, k in stages of 64.  The call's record says which height
+// works: a weight slice is read once per tile, so 256-row tiles halve the
+// weight reads of experts with many pairs, 128-row tiles waste fewer rows on
+// experts with few.  BM / 32 waves, (BM / 64) (rows) x 2 (columns), each
+// 64 x 128 (2 x 4 MFMA tiles of 32 x 32); a wave whose 64 rows are all
+// padding of its expert's last block (or past the last token) skips its LDS
+// reads and MFMAs, and rows past the expert's segment are never stored.  UP: the 256
 // columns are 128 gate rows and the 128 matching up rows of W_gu, so each
 // wave holds gate and up accumulators of the same (position, unit) and
 // applies SiLU(a) * u in registers.  DOWN: A is h (contiguous rows), B is
@@ -47,7 +51,7 @@
 
 namespace beam {
 
-constexpr int GBM = 256;   // rows per expert tile = block_m of the tiled path
+constexpr int GBM = 256;   // rows of the taller expert tile (two 128-row blocks of one expert)
 constexpr int GBM_R = 128; // rows per router tile (more tiles for a 2E-column GEMM)
 constexpr int GBN = 256;   // output columns per tile
 constexpr int GBK = 64;    // k per stage: one 128-byte line per row
@@ -139,7 +143,9 @@ struct GemmArgs {
     int T, d, I, E;
     int n_ntiles;           // column tiles per block
     int n_rblocks;          // ROUTER: row blocks
-    const int32_t *mode;    // UP/DOWN: NULL, or the per-call choice (0: streaming kernels)
+    const int32_t *mode;    // UP/DOWN: the call's record {family, max count, records, 0}
+    const int32_t *pbt;     // UP/DOWN, 256-row tiles: {expert, first position, segment rows,
+                            // valid rows} per tile
 };
 
 template <int MODE, int BM, int NA, int NB, int DKK>
@@ -155,9 +161,9 @@ __global__ __launch_bounds__(BM * 2, 1) void grouped_gemm(GemmArgs g) {
     const int lr = lane & 31;
     const int lh = lane >> 5;
 
-    // this call's experts go to the streaming kernels
-    if (MODE != MODE_ROUTER && g.mode != nullptr && *g.mode == 0) return;
-    const int n_blocks = MODE == MODE_ROUTER ? g.n_rblocks : g.num_active[3];
+    // the call's kernel family: 1 = 128-row tiles, 2 = 256-row tiles (0 = streaming)
+    if (MODE != MODE_ROUTER && g.mode[0] != (BM == 256 ? 2 : 1)) return;
+    const int n_blocks = MODE == MODE_ROUTER ? g.n_rblocks : BM == 256 ? g.mode[2] : g.num_active[3];
     const int n_tiles = n_blocks * g.n_ntiles;
     const int xcd = blockIdx.x & 7;
     const int per_xcd_wg = gridDim.x >> 3;
@@ -186,12 +192,27 @@ __global__ __launch_bounds__(BM * 2, 1) void grouped_gemm(GemmArgs g) {
     for (int tile = t_begin + (int)(blockIdx.x >> 3); tile < t_end; tile += per_xcd_wg) {
         const int blk = tile / g.n_ntiles;
         const int nt = tile - blk * g.n_ntiles;
-        const int pos0 = blk * BM;
-        const int e = MODE == MODE_ROUTER ? 0 : g.block_expert[blk];
-        // rows of this block that hold real pairs (tokens, for the router)
-        const int rows_valid = MODE == MODE_ROUTER
-                                   ? g.T - pos0
-                                   : g.expert_offsets[e] + g.expert_counts[e] - pos0;
+        // tile: BM rows from pos0 of expert e; seg of them lie in the expert's
+        // padded segment (a 256-row tile can end after 128), rows_valid hold
+        // real pairs (tokens, for the router)
+        int pos0, e, seg, rows_valid;
+        if (MODE == MODE_ROUTER) {
+            pos0 = blk * BM;
+            e = 0;
+            seg = BM;
+            rows_valid = g.T - pos0;
+        } else if (BM == 256) {
+            const int4 rec = *reinterpret_cast<const int4 *>(g.pbt + 4 * blk);
+            e = rec.x;
+            pos0 = rec.y;
+            seg = rec.z;
+            rows_valid = rec.w;
+        } else {
+            pos0 = blk * BM;
+            e = g.block_expert[blk];
+            seg = BM;
+            rows_valid = g.expert_offsets[e] + g.expert_counts[e] - pos0;
+        }
         const bool live = __builtin_amdgcn_readfirstlane(wm * 64 < rows_valid ? 1 : 0) != 0;
 
         // this lane's 16 bytes land at slot l % 8 of row r: chunk (l % 8) ^ f(r)
@@ -199,10 +220,13 @@ __global__ __launch_bounds__(BM * 2, 1) void grouped_gemm(GemmArgs g) {
 #pragma unroll
         for (int i = 0; i < C::LA; ++i) {
             const int r = G_RPI * (wave + C::NW * i) + lrow;
+            // rows past the segment (the next expert's, or past the lists)
+            // read the segment's first row; nothing stores them
+            const int rs = r < seg ? r : 0;
             if (MODE == MODE_UP) {
-                srcA[i] = g.A + (size_t)g.sorted_tok[pos0 + r] * g.d;
+                srcA[i] = g.A + (size_t)g.sorted_tok[pos0 + rs] * g.d;
             } else if (MODE == MODE_DOWN) {
-                srcA[i] = g.A + (size_t)(pos0 + r) * g.I;
+                srcA[i] = g.A + (size_t)(pos0 + rs) * g.I;
             } else {
                 const int t = min(pos0 + r, g.T - 1);
                 srcA[i] = g.A + (size_t)t * g.d;
@@ -333,6 +357,7 @@ __global__ __launch_bounds__(BM * 2, 1) void grouped_gemm(GemmArgs g) {
             for (int v = 0; v < 16; ++v) {
                 const int row = wm * 64 + m * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
                 const size_t prow = (size_t)(pos0 + row);
+                if (MODE != MODE_ROUTER && row >= seg) continue;  // the next expert's rows
                 if (MODE == MODE_UP) {
 #pragma unroll
                     for (int n = 0; n < 2; ++n) {
@@ -395,7 +420,8 @@ static GemmArgs base_args(const Plan &p, const Routing &r, const Work &w) {
     a.sorted_tok = w.sorted_tok;
     a.expert_offsets = r.expert_offsets;
     a.expert_counts = r.expert_counts;
-    a.mode = p.split == 0 ? nullptr : w.meta;
+    a.mode = w.meta;
+    a.pbt = w.pbt;
     a.T = p.T;
     a.d = p.d;
     a.I = p.I;
@@ -410,6 +436,9 @@ hipError_t launch_gemm_up(const Plan &p, const void *x, const void *W_gu, const 
     a.W = (const bf16_t *)W_gu;
     a.out = (bf16_t *)w.h;
     a.n_ntiles = p.I / (GBN / 2);
+    // both tile heights; the call's record lets one of them work
+    const hipError_t e = launch_gemm<MODE_UP, 128, 3, 3, 3>(a, s);
+    if (e != hipSuccess) return e;
     return launch_gemm<MODE_UP, GBM, 2, 3, G_DKK>(a, s);
 }
 
@@ -420,6 +449,8 @@ hipError_t launch_gemm_down(const Plan &p, const void *W_dt, const Routing &r, c
     a.W = (const bf16_t *)W_dt;
     a.out = (bf16_t *)w.o;
     a.n_ntiles = p.d / GBN;
+    const hipError_t e = launch_gemm<MODE_DOWN, 128, 3, 3, 3>(a, s);
+    if (e != hipSuccess) return e;
     return launch_gemm<MODE_DOWN, GBM, 2, 3, G_DKK>(a, s);
 }
 

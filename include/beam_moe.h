@@ -70,7 +70,9 @@ extern "C" {
                                          blocks of <= 32 positions per expert
                                          number >= 1.5 x the active experts, or
                                          one expert has > 512 active pairs, else
-                                         the streaming kernels                 */
+                                         the streaming kernels.  Tiled calls use
+                                         128-row tiles while those number < 1.3 x
+                                         the 256-row tiles, else 256-row tiles */
 
 /* stage ids for the optional per-stage events of beam_moe_forward_ex */
 #define BEAM_STAGE_ROUTER   0 /* a1-a4: router logits, top-K, softmax, mask,
@@ -90,8 +92,8 @@ typedef struct beam_moe_desc {
     int32_t  K;        /* top-K                                    (1..E)      */
     int32_t  I;        /* expert intermediate size                 (> 0)       */
     int32_t  dtype;    /* BEAM_F32 or BEAM_BF16                                */
-    int32_t  block_m;  /* 0 = library picks (16 streaming, 256 tiled); else
-                          16, 32, 64, 128 or 256 (the tiled path: 256 only)   */
+    int32_t  block_m;  /* 0 = library picks (16 streaming, 128 tiled); else
+                          16, 32, 64, 128 or 256 (the tiled path: 128 only)   */
     uint32_t flags;    /* BEAM_FORCE_*                                         */
     float    tau;      /* mask threshold on sigmoid(z); 0 means 0.5 (Eq. 6).
                           Evaluated exactly as z >= ln(tau / (1 - tau)).       */

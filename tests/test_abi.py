@@ -85,7 +85,8 @@ def test_query_sizes(T, d, E, K, I, dt):
     (dict(flags=3), B.BEAM_EINVAL), (dict(tau=1.5), B.BEAM_EINVAL),
     (dict(E=300), B.BEAM_EUNSUPPORTED), (dict(d=100), B.BEAM_EUNSUPPORTED),
     (dict(I=48), B.BEAM_EUNSUPPORTED),
-    (dict(I=128, flags=2, block_m=128), B.BEAM_EUNSUPPORTED),
+    (dict(I=128, flags=2, block_m=256), B.BEAM_EUNSUPPORTED),
+    (dict(I=128, flags=2, block_m=64), B.BEAM_EUNSUPPORTED),
     (dict(I=64, flags=2), B.BEAM_EUNSUPPORTED),
 ])
 def test_query_rejects(kw, code):
@@ -98,15 +99,15 @@ def test_query_rejects(kw, code):
 
 
 def test_path_choice():
-    # streaming path up to 512 tokens, tiled path (256-position blocks) above
+    # streaming path up to 512 tokens, tiled path (128-position blocks) above
     assert B.query(B.make_desc(512, 2048, 128, 8, 768, 1))["path"] == 0
     s = B.query(B.make_desc(513, 2048, 128, 8, 768, 1))
-    assert s["path"] == 1 and s["block_m"] == 256
+    assert s["path"] == 1 and s["block_m"] == 128
     # float32 layers and forced decode stay on the streaming path
     assert B.query(B.make_desc(4096, 256, 16, 2, 128, 0))["path"] == 0
     assert B.query(B.make_desc(4096, 2048, 128, 8, 768, 1, flags=1))["path"] == 0
-    s = B.query(B.make_desc(4, 256, 16, 2, 128, 1, flags=2, block_m=256))
-    assert s["path"] == 1 and s["block_m"] == 256
+    s = B.query(B.make_desc(4, 256, 16, 2, 128, 1, flags=2, block_m=128))
+    assert s["path"] == 1 and s["block_m"] == 128
 
 
 def test_reserved_must_be_zero():

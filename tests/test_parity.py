@@ -103,7 +103,8 @@ def test_zero_tokens():
     assert y.shape == (0, 128)
 
 
-# ---- the tiled (prefill) path: grouped MFMA GEMMs over 256-position blocks --
+# ---- the tiled (prefill) path: grouped MFMA GEMMs over 128-position blocks
+# (tiles of 128 rows, or 256 rows = two blocks of one expert) -----------------
 GEMM_SMALL = synth.LayerShape(256, 8, 2, 128, torch.bfloat16)
 
 
@@ -120,7 +121,7 @@ def test_prefill_and_decode_paths_agree():
     L = layer("qwen3", 600, seed=1100, mask_bias=0.0)
     yd, Rd, _ = run(L, 8, flags=B.BEAM_FORCE_DECODE)
     yp, Rp, lay = run(L, 8, flags=B.BEAM_FORCE_PREFILL)
-    assert lay.sizes["path"] == 1 and lay.sizes["block_m"] == 256
+    assert lay.sizes["path"] == 1 and lay.sizes["block_m"] == 128
     np.testing.assert_array_equal(Rd["masked_ids"].numpy(), Rp["masked_ids"].numpy())
     err = np.linalg.norm(yd - yp) / np.linalg.norm(yp)
     assert err < 5e-3
@@ -145,7 +146,53 @@ def test_per_call_kernel_choice(E, tiled):
     assert _expects_tiled(G["counts"]) == tiled
     lay = B.MoELayer(L["W_gate"], L["W_mask"], L["W_gu"], L["W_dt"], 2)
     lay(L["x"])
-    assert lay.sizes["path"] == 1 and lay.sizes["block_m"] == 256
+    assert lay.sizes["path"] == 1 and lay.sizes["block_m"] == 128
+
+
+def _mode_record(lay):
+    """The call's kernel-family record {family, max count, records, 0} from
+    the workspace (layout: tile token sets, tile bases, pair positions, then
+    the record, each piece rounded up to 256 bytes)."""
+    al = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    T, E2, K, S = lay.desc.T, lay.desc.E + lay.desc.n_shared, lay.desc.K, lay.desc.n_shared
+    n_tiles = (T + 63) // 64
+    off = al(n_tiles * E2 * 8) + al(n_tiles * E2 * 4) + al(T * (K + S) * 4)
+    return lay.ws[off:off + 16].view(torch.int32).cpu().numpy()
+
+
+def _expected_family(counts, forced):
+    act = counts[counts > 0]
+    tiled = forced or 2 * ((act + 31) // 32).sum() >= 3 * len(act) or counts.max() > 512
+    if not tiled:
+        return 0
+    n128 = ((act + 127) // 128).sum()
+    n256 = ((act + 255) // 256).sum()
+    return 1 if 10 * n128 < 13 * n256 else 2
+
+
+# ---- the three kernel families: streaming, 128-row tiles, 256-row tiles
+# (including 256-row tiles whose second half lies past the expert's segment)
+@pytest.mark.parametrize("T,forced,b,family", [
+    (300, True, 0.0, 1),      # ~37 pairs per expert: one 128-row tile each
+    (1000, False, -0.3, 1),   # ~95 pairs per expert: tiled by the block rule, 128-row tiles
+    (4096, False, 8.0, 2),    # ~1024 pairs per expert: 256-row tiles (half tiles at odd counts)
+    (900, False, -1.5, 0),    # ~16 pairs per expert: streaming
+])
+def test_kernel_family_choice(T, forced, b, family):
+    import dynamic_expert_sparsity_amd as B
+    shape = synth.LayerShape(256, 16, 4, 128, torch.bfloat16)
+    flags = B.BEAM_FORCE_PREFILL if forced else 0
+    L = layer(shape, T, seed=1400 + T, mask_bias=b)
+    y, G, O, _ = _full_check(L, 4, flags=flags, tokens=sample_tokens(T, 256, seed=T))
+    lay = B.MoELayer(L["W_gate"], L["W_mask"], L["W_gu"], L["W_dt"], 4, flags=flags)
+    lay(L["x"])
+    torch.cuda.synchronize()
+    rec = _mode_record(lay)
+    counts = G["counts"]
+    assert rec[0] == _expected_family(counts, forced)
+    assert rec[0] == family, "the inputs did not land on the intended family"
+    if family == 2:
+        assert rec[2] == ((counts[counts > 0] + 255) // 256).sum()
 
 
 @pytest.mark.parametrize("b", [0.0, 8.0])
