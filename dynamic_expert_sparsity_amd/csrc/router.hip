@@ -10,7 +10,10 @@
 //
 // Kernels: the logits (many workgroups, each a 16-column block), then either
 // one workgroup that selects and groups a small batch, or one workgroup per
-// 64-token tile for the select and one workgroup for the grouping.
+// quarter of a 64-token tile for the select and one workgroup for the
+// grouping.
+#include <type_traits>
+
 #include "compact_dev.h"
 
 namespace beam {
@@ -139,8 +142,9 @@ __global__ __launch_bounds__(256) void router_logits_generic(
 // kept by lane k % LPT.  Softmax over the kept logits shifted by the largest
 // (Eq. 4); the winners' mask logits are gathered afterwards and m = z >= thr
 // (Eq. 6, thr = 0 for tau = 0.5); g_hat = g * m (Eq. 7); id -1 where masked.
-// tmask[e] collects, per 64-token tile, the set of tile tokens with an active
-// pair for expert e; s_mid (optional, LDS) receives the masked ids.
+// tmask[e] collects the set of tokens with an active pair for expert e, bit
+// t % TB for token t (TB = 64: a 64-token tile in 64-bit words; TB = 16: a
+// quarter tile in 32-bit words); s_mid (optional, LDS) receives the masked ids.
 //
 // The group reductions use DPP lane moves: swap neighbours, swap pairs (a
 // quad), then mirror within 8 and within 16 (a row).  Each step combines two
@@ -199,16 +203,19 @@ __device__ __forceinline__ float group_sum(float v) {
 }
 
 // One wavefront: tokens t_first .. t_first + 64/LPT - 1 (all in one tile).
-template <int EJ, int LPT>
-__device__ __forceinline__ void select_group(int T, int E, int K, float thr, const Routing &r,
-                                             unsigned long long *tmask, int *s_mid, int t_first,
-                                             int lane) {
+template <int EJ, int LPT, int TB>
+__device__ __forceinline__ void select_group(
+    int T, int E, int K, float thr, const Routing &r,
+    std::conditional_t<TB == 64, unsigned long long, unsigned> *tmask, int *s_mid, int t_first,
+    int lane) {
+    using MW = std::conditional_t<TB == 64, unsigned long long, unsigned>;
+    static_assert(TB == 64 || TB == 16, "token bits per mask word");
     constexpr int SPL = 16 / LPT;  // slots kept per lane (K <= 16)
     const int i = lane % LPT;
     const int t = t_first + lane / LPT;
     const bool valid = t < T;
     const int tc = valid ? t : T - 1;
-    const int tl = t & 63;
+    const int tl = t & (TB - 1);
     const int e0 = i * EJ;
     // 16-byte loads when every lane's run of EJ logits is 16-byte aligned and whole
     const bool vec = (EJ % 4 == 0) && (E % 4 == 0) && (e0 + EJ <= E);
@@ -284,7 +291,7 @@ __device__ __forceinline__ void select_group(int T, int E, int K, float thr, con
             r.g_hat[o] = m ? g : 0.f;
             r.masked_ids[o] = m ? mye[q] : -1;
             if (s_mid) s_mid[o] = m ? mye[q] : -1;
-            if (m) atomicOr(&tmask[mye[q]], 1ull << tl);
+            if (m) atomicOr(&tmask[mye[q]], (MW)1 << tl);
         }
     }
 }
@@ -295,22 +302,32 @@ __device__ __forceinline__ unsigned long long tile_all(int tile, int T) {
     return n >= 64 ? ~0ull : ((1ull << n) - 1ull);
 }
 
-// One workgroup per 64-token tile: the select, and the tile's token sets for
-// the E routed and S shared experts ([tile][E + S]).
-template <int EJ, int LPT>
-__global__ __launch_bounds__(LPT * 64) void select_topk_mask(int T, int E, int S, int K,
-                                                             float thr, Routing r,
-                                                             uint64_t *__restrict__ tile_mask) {
-    __shared__ unsigned long long tmask[256];
+// One workgroup of four wavefronts per quarter (16 tokens) of a 64-token
+// tile, 16 lanes per token: the select, and the quarter's bits of the tile's
+// token sets for the E routed and S shared experts ([tile][E + S] 64-bit
+// words; bits 16 q .. 16 q + 15 belong to quarter q).  A quarter writes its
+// 16 bits of every word with one 16-bit store, so the words need neither
+// clearing nor atomics across workgroups.  Quarter-tile workgroups spread a
+// batch of a few hundred tokens over four times as many compute units as
+// whole-tile ones: the K dependent arg-max rounds are the select's critical
+// path.
+template <int EJ>
+__global__ __launch_bounds__(256) void select_topk_mask(int T, int E, int S, int K, float thr,
+                                                        Routing r,
+                                                        uint64_t *__restrict__ tile_mask) {
+    __shared__ unsigned tmask[256];
     const int tid = threadIdx.x;
-    for (int e = tid; e < E; e += LPT * 64) tmask[e] = 0ull;
+    for (int e = tid; e < E; e += 256) tmask[e] = 0u;
     __syncthreads();
-    const int t_first = blockIdx.x * 64 + (tid >> 6) * (64 / LPT);
-    if (t_first < T) select_group<EJ, LPT>(T, E, K, thr, r, tmask, nullptr, t_first, tid & 63);
+    const int tile = blockIdx.x >> 2, q = blockIdx.x & 3;
+    const int t_first = blockIdx.x * 16 + (tid >> 6) * 4;
+    if (t_first < T) select_group<EJ, 16, 16>(T, E, K, thr, r, tmask, nullptr, t_first, tid & 63);
     __syncthreads();
     const int E2 = E + S;
-    for (int e = tid; e < E2; e += LPT * 64)
-        tile_mask[(size_t)blockIdx.x * E2 + e] = e < E ? tmask[e] : tile_all(blockIdx.x, T);
+    // 16-bit field q of word [tile][e]
+    uint16_t *dst = reinterpret_cast<uint16_t *>(tile_mask + (size_t)tile * E2) + q;
+    for (int e = tid; e < E2; e += 256)
+        dst[4 * e] = (uint16_t)(e < E ? tmask[e] : tile_all(tile, T) >> (16 * q));
 }
 
 // The grouping of a batch of tiles by one workgroup (and the pair positions
@@ -350,7 +367,7 @@ __global__ __launch_bounds__(1024) void route_small(int T, int E, int S, int K, 
     if (tid < E) tmask[tid] = 0ull;
     __syncthreads();
     for (int t_first = (tid >> 6) * TPW; t_first < T; t_first += 16 * TPW)
-        select_group<EJ, LPT>(T, E, K, thr, r, tmask, s_mid, t_first, tid & 63);
+        select_group<EJ, LPT, 64>(T, E, K, thr, r, tmask, s_mid, t_first, tid & 63);
     __syncthreads();
     if (tid < E2) s_cnt[tid] = tid < E ? __popcll(tmask[tid]) : T;
     __syncthreads();
@@ -379,9 +396,9 @@ static void launch_select_t(const Plan &p, const Routing &r, const Work &w, hipS
     if (p.T <= 64) {
         route_small<EJ, LPT><<<1, 1024, 0, s>>>(p.T, p.E, p.S, p.K, p.thr, p.bm, r, w.pair_pos,
                                                w.meta, w.sorted_tok, w.pbt, p.split);
-    } else {
-        select_topk_mask<EJ, LPT><<<p.n_tiles, LPT * 64, 0, s>>>(p.T, p.E, p.S, p.K, p.thr, r,
-                                                               w.tile_mask);
+    } else if constexpr (LPT == 16) {
+        select_topk_mask<EJ><<<p.n_tiles * 4, 256, 0, s>>>(p.T, p.E, p.S, p.K, p.thr, r,
+                                                          w.tile_mask);
         compact_tiles<<<1, 1024, 0, s>>>(w.tile_mask, p.n_tiles, p.E, p.S, p.bm, p.K, p.T * p.K,
                                          r, w.tile_base, w.pair_pos, w.meta, w.sorted_tok, w.pbt,
                                          p.fuse_scatter, p.split);
@@ -445,9 +462,10 @@ hipError_t launch_route(const Plan &p, const void *x, const void *Wg, const void
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    // few tokens: 16 select lanes per token (shortest latency); more: 4 lanes
-    // per token (a quarter of the instructions per token)
-    if (p.T <= 32) launch_select_l<16>(p, r, w, s);
+    // one workgroup for at most 64 tokens: 16 select lanes per token up to 32
+    // tokens (shortest latency), else 4 (a quarter of the instructions per
+    // token); more tokens: quarter-tile workgroups, 16 lanes per token
+    if (p.T <= 32 || p.T > 64) launch_select_l<16>(p, r, w, s);
     else launch_select_l<4>(p, r, w, s);
     return hipGetLastError();
 }
