@@ -134,12 +134,11 @@ __global__ __launch_bounds__(256) void router_logits_generic(
 }
 
 // ---------------------------------------------------------------------------
-// Select (Eq. 4-7 per token).  A token is handled by LPT lanes of one
-// wavefront (LPT = 4 or 16, a DPP quad or row); lane i of the group holds the
-// gate logits of experts i*EJ .. i*EJ+EJ-1, so a wavefront handles 64/LPT
-// consecutive tokens.  K rounds of a group-wide arg-max under the key
-// (value desc, expert asc) give the Top-K slots in order (Eq. 4); slot k is
-// kept by lane k % LPT.  Softmax over the kept logits shifted by the largest
+// Select (Eq. 4-7 per token).  A token is handled by the 16 lanes of one DPP
+// row of a wavefront; lane i of the row holds the gate logits of experts
+// i*EJ .. i*EJ+EJ-1, so a wavefront handles 4 consecutive tokens.  K rounds
+// of a row-wide arg-max under the key (value desc, expert asc) give the Top-K
+// slots in order (Eq. 4); slot k (K <= 16) is kept by lane k.  Softmax over the kept logits shifted by the largest
 // (Eq. 4); the winners' mask logits are gathered afterwards and m = z >= thr
 // (Eq. 6, thr = 0 for tau = 0.5); g_hat = g * m (Eq. 7); id -1 where masked.
 // tmask[e] collects the set of tokens with an active pair for expert e, bit
@@ -181,38 +180,32 @@ __device__ __forceinline__ void argmax_step(float &bv, int &be) {
     }
 }
 
-template <int LPT>
-__device__ __forceinline__ void group_argmax(float &bv, int &be) {
+__device__ __forceinline__ void row_argmax(float &bv, int &be) {
     argmax_step<DPP_QUAD_1032>(bv, be);
     argmax_step<DPP_QUAD_2301>(bv, be);
-    if constexpr (LPT == 16) {
-        argmax_step<DPP_ROW_HALF_MIRROR>(bv, be);
-        argmax_step<DPP_ROW_MIRROR>(bv, be);
-    }
+    argmax_step<DPP_ROW_HALF_MIRROR>(bv, be);
+    argmax_step<DPP_ROW_MIRROR>(bv, be);
 }
 
-template <int LPT>
-__device__ __forceinline__ float group_sum(float v) {
+__device__ __forceinline__ float row_sum(float v) {
     v += dpp_f<DPP_QUAD_1032>(v);
     v += dpp_f<DPP_QUAD_2301>(v);
-    if constexpr (LPT == 16) {
-        v += dpp_f<DPP_ROW_HALF_MIRROR>(v);
-        v += dpp_f<DPP_ROW_MIRROR>(v);
-    }
+    v += dpp_f<DPP_ROW_HALF_MIRROR>(v);
+    v += dpp_f<DPP_ROW_MIRROR>(v);
     return v;
 }
 
-// One wavefront: tokens t_first .. t_first + 64/LPT - 1 (all in one tile).
-template <int EJ, int LPT, int TB>
+// One wavefront: tokens t_first .. t_first + 3 (all in one tile).
+template <int EJ, int TB>
 __device__ __forceinline__ void select_group(
     int T, int E, int K, float thr, const Routing &r,
     std::conditional_t<TB == 64, unsigned long long, unsigned> *tmask, int *s_mid, int t_first,
     int lane) {
     using MW = std::conditional_t<TB == 64, unsigned long long, unsigned>;
     static_assert(TB == 64 || TB == 16, "token bits per mask word");
-    constexpr int SPL = 16 / LPT;  // slots kept per lane (K <= 16)
-    const int i = lane % LPT;
-    const int t = t_first + lane / LPT;
+    static_assert(EJ >= 1 && EJ <= 16, "at most 16 experts per lane (E <= 256)");
+    const int i = lane & 15;
+    const int t = t_first + (lane >> 4);
     const bool valid = t < T;
     const int tc = valid ? t : T - 1;
     const int tl = t & (TB - 1);
@@ -235,65 +228,49 @@ __device__ __forceinline__ void select_group(
 #pragma unroll
         for (int j = 0; j < EJ; ++j) rv[j] = e0 + j < E ? gr[j] : 0.f;
     }
-    uint64_t live = 0;
+    unsigned live = 0;
 #pragma unroll
     for (int j = 0; j < EJ; ++j)
-        if (e0 + j < E) live |= 1ull << j;
+        if (e0 + j < E) live |= 1u << j;
 
-    float v0 = 0.f, myv[SPL];
-    int mye[SPL];
-#pragma unroll
-    for (int q = 0; q < SPL; ++q) {
-        myv[q] = 0.f;
-        mye[q] = 0;
-    }
+    // slot k is kept by lane k
+    float v0 = 0.f, myv = 0.f;
+    int mye = 0;
     for (int k = 0; k < K; ++k) {
         float bv = 0.f;
         int be = NO_EXPERT;
 #pragma unroll
         for (int j = 0; j < EJ; ++j) {  // expert index ascends with j: ties keep the first
-            if (((live >> j) & 1ull) && (be == NO_EXPERT || rv[j] > bv)) {
+            if (((live >> j) & 1u) && (be == NO_EXPERT || rv[j] > bv)) {
                 bv = rv[j];
                 be = e0 + j;
             }
         }
-        group_argmax<LPT>(bv, be);
+        row_argmax(bv, be);
         const int jw = be - e0;
-        if (jw >= 0 && jw < EJ) live &= ~(1ull << jw);
+        if (jw >= 0 && jw < EJ) live &= ~(1u << jw);
         if (k == 0) v0 = bv;
-#pragma unroll
-        for (int q = 0; q < SPL; ++q)
-            if (k == i + LPT * q) {
-                myv[q] = bv;
-                mye[q] = be;
-            }
-    }
-
-    float num[SPL], part = 0.f;
-#pragma unroll
-    for (int q = 0; q < SPL; ++q) {
-        num[q] = i + LPT * q < K ? expf(myv[q] - v0) : 0.f;
-        part += num[q];
-    }
-    const float den = group_sum<LPT>(part);
-    if (!valid) return;
-#pragma unroll
-    for (int q = 0; q < SPL; ++q) {
-        const int k = i + LPT * q;
-        if (k < K) {
-            const float z = r.mask_logits[(size_t)t * E + mye[q]];
-            const float g = num[q] / den;
-            const bool m = z >= thr;
-            const int o = t * K + k;
-            r.topk_ids[o] = mye[q];
-            r.topk_weights[o] = g;
-            r.mask[o] = m ? 1 : 0;
-            r.g_hat[o] = m ? g : 0.f;
-            r.masked_ids[o] = m ? mye[q] : -1;
-            if (s_mid) s_mid[o] = m ? mye[q] : -1;
-            if (m) atomicOr(&tmask[mye[q]], (MW)1 << tl);
+        if (k == i) {
+            myv = bv;
+            mye = be;
         }
     }
+
+    const float num = i < K ? expf(myv - v0) : 0.f;
+    const float den = row_sum(num);
+    if (!valid || i >= K) return;
+    const int k = i;
+    const float z = r.mask_logits[(size_t)t * E + mye];
+    const float g = num / den;
+    const bool m = z >= thr;
+    const int o = t * K + k;
+    r.topk_ids[o] = mye;
+    r.topk_weights[o] = g;
+    r.mask[o] = m ? 1 : 0;
+    r.g_hat[o] = m ? g : 0.f;
+    r.masked_ids[o] = m ? mye : -1;
+    if (s_mid) s_mid[o] = m ? mye : -1;
+    if (m) atomicOr(&tmask[mye], (MW)1 << tl);
 }
 
 // The token set of tile `tile` for a shared expert: every valid token.
@@ -321,7 +298,7 @@ __global__ __launch_bounds__(256) void select_topk_mask(int T, int E, int S, int
     __syncthreads();
     const int tile = blockIdx.x >> 2, q = blockIdx.x & 3;
     const int t_first = blockIdx.x * 16 + (tid >> 6) * 4;
-    if (t_first < T) select_group<EJ, 16, 16>(T, E, K, thr, r, tmask, nullptr, t_first, tid & 63);
+    if (t_first < T) select_group<EJ, 16>(T, E, K, thr, r, tmask, nullptr, t_first, tid & 63);
     __syncthreads();
     const int E2 = E + S;
     // 16-bit field q of word [tile][e]
@@ -351,7 +328,7 @@ __global__ __launch_bounds__(1024) void compact_tiles(const uint64_t *__restrict
 // A small batch (T <= 64, one tile) in one workgroup: select, counts,
 // offsets, lists and pair positions of the E routed and S shared experts;
 // the token sets and masked ids stay in LDS.
-template <int EJ, int LPT>
+template <int EJ>
 __global__ __launch_bounds__(1024) void route_small(int T, int E, int S, int K, float thr, int bm,
                                                     Routing r, int32_t *__restrict__ pair_pos,
                                                     int32_t *__restrict__ meta,
@@ -361,13 +338,13 @@ __global__ __launch_bounds__(1024) void route_small(int T, int E, int S, int K, 
     __shared__ int s_mid[64 * 16];
     __shared__ int s_cnt[256];
     __shared__ int s_off[257];
-    constexpr int TPW = 64 / LPT;  // tokens per wavefront
     const int tid = threadIdx.x;
     const int E2 = E + S;
     if (tid < E) tmask[tid] = 0ull;
     __syncthreads();
-    for (int t_first = (tid >> 6) * TPW; t_first < T; t_first += 16 * TPW)
-        select_group<EJ, LPT, 64>(T, E, K, thr, r, tmask, s_mid, t_first, tid & 63);
+    // 16 waves of 4 tokens: one pass over a 64-token tile
+    const int t_first = (tid >> 6) * 4;
+    if (t_first < T) select_group<EJ, 64>(T, E, K, thr, r, tmask, s_mid, t_first, tid & 63);
     __syncthreads();
     if (tid < E2) s_cnt[tid] = tid < E ? __popcll(tmask[tid]) : T;
     __syncthreads();
@@ -391,12 +368,20 @@ __global__ __launch_bounds__(1024) void route_small(int T, int E, int S, int K, 
     }
 }
 
-template <int EJ, int LPT>
+// A batch of at most BEAM_SMALL_T tokens (one 64-token tile) is routed by
+// one workgroup; a larger one by quarter-tile select workgroups and one
+// grouping workgroup.
+#ifndef BEAM_SMALL_T
+#define BEAM_SMALL_T 64
+#endif
+static_assert(BEAM_SMALL_T <= 64, "route_small holds one 64-token tile");
+
+template <int EJ>
 static void launch_select_t(const Plan &p, const Routing &r, const Work &w, hipStream_t s) {
-    if (p.T <= 64) {
-        route_small<EJ, LPT><<<1, 1024, 0, s>>>(p.T, p.E, p.S, p.K, p.thr, p.bm, r, w.pair_pos,
-                                               w.meta, w.sorted_tok, w.pbt, p.split);
-    } else if constexpr (LPT == 16) {
+    if (p.T <= BEAM_SMALL_T) {
+        route_small<EJ><<<1, 1024, 0, s>>>(p.T, p.E, p.S, p.K, p.thr, p.bm, r, w.pair_pos, w.meta,
+                                           w.sorted_tok, w.pbt, p.split);
+    } else {
         select_topk_mask<EJ><<<p.n_tiles * 4, 256, 0, s>>>(p.T, p.E, p.S, p.K, p.thr, r,
                                                           w.tile_mask);
         compact_tiles<<<1, 1024, 0, s>>>(w.tile_mask, p.n_tiles, p.E, p.S, p.bm, p.K, p.T * p.K,
@@ -405,21 +390,19 @@ static void launch_select_t(const Plan &p, const Routing &r, const Work &w, hipS
     }
 }
 
-template <int LPT>
-static void launch_select_l(const Plan &p, const Routing &r, const Work &w, hipStream_t s) {
-    // experts per select lane: E / LPT rounded up to a power of two
-    const int ej = (p.E + LPT - 1) / LPT;
-    if (ej <= 1) launch_select_t<1, LPT>(p, r, w, s);
-    else if (ej <= 2) launch_select_t<2, LPT>(p, r, w, s);
-    else if (ej <= 4) launch_select_t<4, LPT>(p, r, w, s);
-    else if (ej <= 8) launch_select_t<8, LPT>(p, r, w, s);
-    else if (ej <= 16) launch_select_t<16, LPT>(p, r, w, s);
-    else if constexpr (LPT == 4) {
-        if (ej <= 32) launch_select_t<32, LPT>(p, r, w, s);
-        else launch_select_t<64, LPT>(p, r, w, s);
-    }
+static void launch_select(const Plan &p, const Routing &r, const Work &w, hipStream_t s) {
+    // experts per select lane (16 lanes per token), rounded up to a power of two
+    const int ej = (p.E + 15) / 16;
+    if (ej <= 1) launch_select_t<1>(p, r, w, s);
+    else if (ej <= 2) launch_select_t<2>(p, r, w, s);
+    else if (ej <= 4) launch_select_t<4>(p, r, w, s);
+    else if (ej <= 8) launch_select_t<8>(p, r, w, s);
+    else launch_select_t<16>(p, r, w, s);
 }
 
+#ifndef BEAM_ROUTER_NARROW_T
+#define BEAM_ROUTER_NARROW_T 256
+#endif
 #ifndef BEAM_ROUTER_GEMM_T
 #define BEAM_ROUTER_GEMM_T 2048
 #endif
@@ -434,10 +417,11 @@ hipError_t launch_route(const Plan &p, const void *x, const void *Wg, const void
         hipError_t err = launch_gemm_router(p, x, Wg, Wm, r, s);
         if (err != hipSuccess) return err;
     } else if (p.dtype == 1) {
-        // few tokens: 16-token tiles of one column block (the most
-        // workgroups); more: 32-token tiles; large batches: 64-token tiles of
-        // four column blocks, so x and the weights are each re-read fewer times
-        const int mt = p.T <= 16 ? 1 : p.T <= BEAM_ROUTER_WIDE_T ? 2 : 4;
+        // up to a few hundred tokens: 16-token tiles of one column block (the
+        // most workgroups, the fewest bytes per workgroup); more: 32-token
+        // tiles; large batches: 64-token tiles of four column blocks, so x and
+        // the weights are each re-read fewer times
+        const int mt = p.T <= BEAM_ROUTER_NARROW_T ? 1 : p.T <= BEAM_ROUTER_WIDE_T ? 2 : 4;
         const int ncb = p.T <= BEAM_ROUTER_WIDE_T ? 1 : 4;
         const dim3 grid((p.T + 16 * mt - 1) / (16 * mt), (2 * p.E + 16 * ncb - 1) / (16 * ncb));
 #define BEAM_ROUTER(MTV, NWV, NCV)                                                             \
@@ -462,11 +446,7 @@ hipError_t launch_route(const Plan &p, const void *x, const void *Wg, const void
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    // one workgroup for at most 64 tokens: 16 select lanes per token up to 32
-    // tokens (shortest latency), else 4 (a quarter of the instructions per
-    // token); more tokens: quarter-tile workgroups, 16 lanes per token
-    if (p.T <= 32 || p.T > 64) launch_select_l<16>(p, r, w, s);
-    else launch_select_l<4>(p, r, w, s);
+    launch_select(p, r, w, s);
     return hipGetLastError();
 }
 
