@@ -404,7 +404,7 @@ static void launch_select(const Plan &p, const Routing &r, const Work &w, hipStr
 #define BEAM_ROUTER_NARROW_T 256
 #endif
 #ifndef BEAM_ROUTER_GEMM_T
-#define BEAM_ROUTER_GEMM_T 2048
+#define BEAM_ROUTER_GEMM_T 8192
 #endif
 #ifndef BEAM_ROUTER_WIDE_T
 #define BEAM_ROUTER_WIDE_T 1024

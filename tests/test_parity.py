@@ -201,6 +201,14 @@ def test_qwen3_prefill_8192(b):
     _full_check(L, 8, tokens=sample_tokens(8192, 32, seed=2))
 
 
+# above 8192 tokens the logits come from the router GEMM (128-token tiles):
+# last tiles holding 1 and 108 tokens (every logit and route is checked)
+@pytest.mark.parametrize("T", [8193, 8300])
+def test_router_gemm_ragged(T):
+    L = layer(SMALL, T, seed=1250 + T, mask_bias=0.0)
+    _full_check(L, 2, tokens=sample_tokens(T, 32, seed=5))
+
+
 @pytest.mark.parametrize("T,b", [(1, -1.04), (64, 0.0), (4096, -1.04)])
 def test_large_layer(T, b):
     L = layer("large", T, seed=1300 + T, mask_bias=b)
