@@ -10,8 +10,9 @@
 // output columns, k in stages of 64.  The call's record says which height
 // works: a weight slice is read once per tile, so 256-row tiles halve the
 // weight reads of experts with many pairs, 128-row tiles waste fewer rows on
-// experts with few.  BM / 32 waves, (BM / 64) (rows) x 2 (columns), each
-// 64 x 128 (2 x 4 MFMA tiles of 32 x 32); a wave whose 64 rows are all
+// experts with few.  (BM / WT) (rows) x 2 (columns) waves, each WT x 128
+// (WT / 32 x 4 MFMA tiles of 32 x 32; WT = 64 for the 256-row and router
+// tiles, 32 for the 128-row expert tiles); a wave whose WT rows are all
 // padding of its expert's last block (or past the last token) skips its LDS
 // reads and MFMAs, and rows past the expert's segment are never stored.  UP: the 256
 // columns are 128 gate rows and the 128 matching up rows of W_gu, so each
@@ -61,14 +62,26 @@ constexpr int G_RPI = 1024 / G_ROWB;  // rows per 1 KB wave load (8)
 #ifndef G_DKK
 #define G_DKK 4
 #endif
+// the 128-row tiles: rows per wave (32: eight waves, each 32 x 128, half
+// the DMA issues per wave of four 64-row waves; 6-7 us faster down
+// projections at 70-80 pairs per expert) and the k-slices their loads are
+// spread over
+#ifndef G_WT128
+#define G_WT128 32
+#endif
+#ifndef G_DKK128
+#define G_DKK128 3
+#endif
 
-// BM rows per tile (BM / 32 waves, each 64 x 128); A in a ring of NA
-// stages, B in a ring of NB (NA or NA + 1) stages; a stage's loads are spread
-// over DKK of its four k-slices
-template <int BM, int NA, int NB, int DKK>
+// BM rows per tile, WT rows per wave (BM / WT x 2 waves, each WT x 128);
+// A in a ring of NA stages, B in a ring of NB (NA or NA + 1) stages; a
+// stage's loads are spread over DKK of its four k-slices
+template <int BM, int NA, int NB, int DKK, int WT>
 struct GemmCfg {
-    static constexpr int WM = BM / 64;                      // waves along the rows
+    static constexpr int WM = BM / WT;                      // waves along the rows
     static constexpr int NW = WM * 2;                       // waves per workgroup
+    static constexpr int MF = WT / 32;                      // 32-row MFMA tiles per wave
+    static constexpr int MPS = MF * 4;                      // MFMAs per wave per k-slice
     static constexpr int A_BYTES = BM * G_ROWB;             // one stage of A
     static constexpr int B_BYTES = GBN * G_ROWB;            // one stage of B
     static constexpr int B_OFF = NA * A_BYTES;              // B ring after the A ring
@@ -81,7 +94,8 @@ struct GemmCfg {
     static_assert(LA * NW * 1024 == A_BYTES && LB * NW * 1024 == B_BYTES, "whole wave loads");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     static_assert((NA == 2 && NB == 3) || (NA == 3 && NB == 3), "ring depths");
-    static_assert(PER * DKK == L && 8 % PER == 0 && DKK <= KK, "load spread");
+    static_assert(PER * DKK == L && MPS % PER == 0 && DKK <= KK, "load spread");
+    static_assert(WT == 32 || WT == 64 || WT == 128, "wave tile height");
     // Issue slot p (stage p of the loop; p < 0 before it) sends A of stage
     // p + NA - 1, then B of stage p + NB - 1; load u goes out in k-slice
     // u / PER, and slice KK - 1 runs after the boundary p -> p + 1.  Loads
@@ -148,9 +162,10 @@ struct GemmArgs {
                             // valid rows} per tile
 };
 
-template <int MODE, int BM, int NA, int NB, int DKK>
-__global__ __launch_bounds__(BM * 2, 1) void grouped_gemm(GemmArgs g) {
-    using C = GemmCfg<BM, NA, NB, DKK>;
+template <int MODE, int BM, int NA, int NB, int DKK, int WT>
+__global__ __launch_bounds__(BM / WT * 128, 1) void grouped_gemm(GemmArgs g) {
+    using C = GemmCfg<BM, NA, NB, DKK, WT>;
+    constexpr int MF = C::MF;
     constexpr int KK = C::KK;  // 16-wide k-slices per stage
     static_assert(KK % 2 == 0, "fragment sets alternate by slice parity");
     extern __shared__ __align__(16) unsigned char lds[];
@@ -213,7 +228,7 @@ __global__ __launch_bounds__(BM * 2, 1) void grouped_gemm(GemmArgs g) {
             seg = BM;
             rows_valid = g.expert_offsets[e] + g.expert_counts[e] - pos0;
         }
-        const bool live = __builtin_amdgcn_readfirstlane(wm * 64 < rows_valid ? 1 : 0) != 0;
+        const bool live = __builtin_amdgcn_readfirstlane(wm * WT < rows_valid ? 1 : 0) != 0;
 
         // this lane's 16 bytes land at slot l % 8 of row r: chunk (l % 8) ^ f(r)
         const bf16_t *srcA[C::LA], *srcB[C::LB];
@@ -264,41 +279,42 @@ __global__ __launch_bounds__(BM * 2, 1) void grouped_gemm(GemmArgs g) {
             }
         };
 
-        f32x16 acc[2][4];
+        f32x16 acc[MF][4];
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+        for (int m = 0; m < MF; ++m)
 #pragma unroll
             for (int n = 0; n < 4; ++n)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[m][n][v] = 0.f;
 
         // fragments of one 16-wide k-slice, in two alternating sets
-        u32x4 af[2][2], bfr[2][4];
+        u32x4 af[2][MF], bfr[2][4];
         auto read_frags = [&](int s, int kk, int set) {
             const unsigned char *sa = lds + (s % NA) * C::A_BYTES;
             const unsigned char *sb = lds + C::B_OFF + (s % NB) * C::B_BYTES;
             const int ch = 2 * kk + lh;
 #pragma unroll
-            for (int m = 0; m < 2; ++m)
-                af[set][m] = *reinterpret_cast<const u32x4 *>(sa + swz(wm * 64 + m * 32 + lr, ch));
+            for (int m = 0; m < MF; ++m)
+                af[set][m] = *reinterpret_cast<const u32x4 *>(sa + swz(wm * WT + m * 32 + lr, ch));
 #pragma unroll
             for (int n = 0; n < 4; ++n)
                 bfr[set][n] = *reinterpret_cast<const u32x4 *>(sb + swz(brow[n] + lr, ch));
         };
-        // one k-slice of stage s: the 8 MFMAs (LIVE waves) with the loads of
-        // issue slot s interleaved (spread over the first DKK slices, one
-        // after every few MFMAs, so the address unit works while the matrix
-        // cores do)
+        // one k-slice of stage s: the MF x 4 MFMAs (LIVE waves) with the
+        // loads of issue slot s interleaved (spread over the first DKK
+        // slices, one after every few MFMAs, so the address unit works while
+        // the matrix cores do)
         constexpr int PER = C::PER;
+        constexpr int MPS = C::MPS;
         auto slice = [&](auto LIVE, int set, int s, int kk) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < MPS; ++j) {
                 const int m = j >> 2, n = j & 3;
                 if constexpr (decltype(LIVE)::value)
                     acc[m][n] = mfma32x32x16(af[set][m], bfr[set][n], acc[m][n]);
-                if (kk < DKK && (j % (8 / PER)) == 0) {
+                if (kk < DKK && (j % (MPS / PER)) == 0) {
                     __builtin_amdgcn_sched_barrier(0);
-                    issue(s, kk * PER + j / (8 / PER));
+                    issue(s, kk * PER + j / (MPS / PER));
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -338,8 +354,9 @@ __global__ __launch_bounds__(BM * 2, 1) void grouped_gemm(GemmArgs g) {
                         if constexpr (LV) read_frags(s + 1, 0, 0);
                     }
                     // the slice's own fragments are in (LDS reads complete in
-                    // order; only the 6 reads of the next slice may be pending)
-                    if constexpr (LV) wait_lgkm<6>();
+                    // order; only the MF + 4 reads of the next slice may be
+                    // pending)
+                    if constexpr (LV) wait_lgkm<MF + 4>();
                     __builtin_amdgcn_sched_barrier(0);
                     slice(LIVE, kk & 1, s, kk);
                 }
@@ -352,10 +369,10 @@ __global__ __launch_bounds__(BM * 2, 1) void grouped_gemm(GemmArgs g) {
         // register 4*(i/8) + i%4.  Pad rows of a block compute values nothing
         // reads (their A rows are token 0 / h rows inside the buffer).
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
+        for (int m = 0; m < MF; ++m) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int row = wm * 64 + m * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+                const int row = wm * WT + m * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
                 const size_t prow = (size_t)(pos0 + row);
                 if (MODE != MODE_ROUTER && row >= seg) continue;  // the next expert's rows
                 if (MODE == MODE_UP) {
@@ -399,17 +416,17 @@ static int persistent_wgs() {
     return n;
 }
 
-template <int MODE, int BM, int NA, int NB, int DKK>
+template <int MODE, int BM, int NA, int NB, int DKK, int WT>
 static hipError_t launch_gemm(const GemmArgs &a, hipStream_t s) {
     static std::once_flag once;
     static hipError_t attr_err = hipSuccess;
-    using C = GemmCfg<BM, NA, NB, DKK>;
+    using C = GemmCfg<BM, NA, NB, DKK, WT>;
     std::call_once(once, [] {
-        attr_err = hipFuncSetAttribute((const void *)grouped_gemm<MODE, BM, NA, NB, DKK>,
+        attr_err = hipFuncSetAttribute((const void *)grouped_gemm<MODE, BM, NA, NB, DKK, WT>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
     });
     if (attr_err != hipSuccess) return attr_err;
-    grouped_gemm<MODE, BM, NA, NB, DKK><<<persistent_wgs(), C::NW * 64, C::LDS_BYTES, s>>>(a);
+    grouped_gemm<MODE, BM, NA, NB, DKK, WT><<<persistent_wgs(), C::NW * 64, C::LDS_BYTES, s>>>(a);
     return hipGetLastError();
 }
 
@@ -437,9 +454,9 @@ hipError_t launch_gemm_up(const Plan &p, const void *x, const void *W_gu, const 
     a.out = (bf16_t *)w.h;
     a.n_ntiles = p.I / (GBN / 2);
     // both tile heights; the call's record lets one of them work
-    const hipError_t e = launch_gemm<MODE_UP, 128, 3, 3, 3>(a, s);
+    const hipError_t e = launch_gemm<MODE_UP, 128, 3, 3, G_DKK128, G_WT128>(a, s);
     if (e != hipSuccess) return e;
-    return launch_gemm<MODE_UP, GBM, 2, 3, G_DKK>(a, s);
+    return launch_gemm<MODE_UP, GBM, 2, 3, G_DKK, 64>(a, s);
 }
 
 hipError_t launch_gemm_down(const Plan &p, const void *W_dt, const Routing &r, const Work &w,
@@ -449,9 +466,9 @@ hipError_t launch_gemm_down(const Plan &p, const void *W_dt, const Routing &r, c
     a.W = (const bf16_t *)W_dt;
     a.out = (bf16_t *)w.o;
     a.n_ntiles = p.d / GBN;
-    const hipError_t e = launch_gemm<MODE_DOWN, 128, 3, 3, 3>(a, s);
+    const hipError_t e = launch_gemm<MODE_DOWN, 128, 3, 3, G_DKK128, G_WT128>(a, s);
     if (e != hipSuccess) return e;
-    return launch_gemm<MODE_DOWN, GBM, 2, 3, G_DKK>(a, s);
+    return launch_gemm<MODE_DOWN, GBM, 2, 3, G_DKK, 64>(a, s);
 }
 
 hipError_t launch_gemm_router(const Plan &p, const void *x, const void *Wg, const void *Wm,
@@ -467,7 +484,7 @@ hipError_t launch_gemm_router(const Plan &p, const void *x, const void *Wg, cons
     a.E = p.E;
     a.n_ntiles = (2 * p.E + GBN - 1) / GBN;
     a.n_rblocks = (p.T + GBM_R - 1) / GBM_R;
-    return launch_gemm<MODE_ROUTER, GBM_R, 3, 3, 3>(a, s);
+    return launch_gemm<MODE_ROUTER, GBM_R, 3, 3, 3, 64>(a, s);
 }
 
 }  // namespace beam
