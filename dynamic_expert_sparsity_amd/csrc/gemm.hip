@@ -62,6 +62,9 @@ constexpr int G_RPI = 1024 / G_ROWB;  // rows per 1 KB wave load (8)
 #ifndef G_DKK
 #define G_DKK 4
 #endif
+#ifndef G_SKIP_A
+#define G_SKIP_A 1
+#endif
 // the 128-row tiles: rows per wave (32: eight waves, each 32 x 128, half
 // the DMA issues per wave of four 64-row waves; 6-7 us faster down
 // projections at 70-80 pairs per expert) and the k-slices their loads are
@@ -265,10 +268,22 @@ __global__ __launch_bounds__(BM / WT * 128, 1) void grouped_gemm(GemmArgs g) {
         // issue slot p (stage p of the loop; p < 0 before it) loads A of stage
         // p + NA - 1 and then B of stage p + NB - 1, each into the ring buffer
         // the stage before it left free at the last boundary
+        // A loads whose 8 rows all lie past the tile's valid rows are not
+        // sent (SKIP_A): no MFMA result that is stored for a real pair reads
+        // them (a row's products depend on that row only; pad rows of a
+        // segment are written but never read), and with NB = NA + 1 every
+        // wait allows only B loads to be outstanding, which are always sent
+        // (so a missing A load never shortens a wait).  Keeps the weight
+        // stream and drops the DMA of a part-filled tile's empty rows.
+        constexpr bool SKIP_A = G_SKIP_A && MODE != MODE_ROUTER && NB == NA + 1;
+        unsigned a_send = 0;  // bit u: A load u has a valid row (wave-uniform)
+#pragma unroll
+        for (int i = 0; i < C::LA; ++i)
+            if (!SKIP_A || G_RPI * (wave + C::NW * i) < rows_valid) a_send |= 1u << i;
         auto issue = [&](int p, int u) {
             if (u < C::LA) {
                 const int j = p + NA - 1;
-                if (j >= 0 && j < nst)
+                if (j >= 0 && j < nst && ((a_send >> u) & 1u))
                     lds_dma16(srcA[u] + j * GBK,
                               lds + (j % NA) * C::A_BYTES + (wave + C::NW * u) * 1024);
             } else {
