@@ -17,8 +17,10 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int BLOCK = 256;
-constexpr int PER_THREAD = 16;  // 16-byte elements per thread, BLOCK apart
+constexpr int BLOCK = 256;      // threads of the copy's and the MFMA loop's workgroups
+constexpr int SBLOCK = 512;     // threads of the read's workgroups
+constexpr int PER_THREAD = 16;  // 16-byte elements per thread per round
+constexpr int ROUND = SBLOCK * PER_THREAD;  // elements of a workgroup round (128 KB)
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
@@ -31,9 +33,10 @@ int cu_count() {
     return cus;
 }
 
-// Workgroup b copies the contiguous elements [b*BLOCK*PER_THREAD, ...) of n
-// 16-byte elements: every wave instruction moves 1 KB, all PER_THREAD loads
-// of a thread are in flight before its stores.
+// Copy: workgroup b copies the contiguous elements [b*BLOCK*PER_THREAD, ...)
+// of n 16-byte elements: every wave instruction moves 1 KB, all PER_THREAD
+// loads of a thread are in flight before its stores (one round per
+// workgroup measured faster than persistent workgroups for the copy).
 __global__ __launch_bounds__(BLOCK) void copy16(const u32x4_t *__restrict__ src,
                                                 u32x4_t *__restrict__ dst, size_t n) {
     const size_t base = (size_t)blockIdx.x * BLOCK * PER_THREAD + threadIdx.x;
@@ -50,21 +53,27 @@ __global__ __launch_bounds__(BLOCK) void copy16(const u32x4_t *__restrict__ src,
     }
 }
 
-// Reads n 16-byte elements in the same order; the xor of everything a
-// thread read is stored only if it equals a value that the caller's data
-// does not produce in practice, so the loads stay and nothing is written.
-__global__ __launch_bounds__(BLOCK) void read16(const u32x4_t *__restrict__ src, size_t n,
-                                                u32x4_t *__restrict__ sink) {
-    const size_t base = (size_t)blockIdx.x * BLOCK * PER_THREAD + threadIdx.x;
-    u32x4_t v[PER_THREAD];
+// Read: persistent workgroups (two per CU); workgroup b takes the 128 KB
+// rounds b, b + G, ... of the n 16-byte elements, so at any time the grid
+// works through one contiguous window; every wave instruction moves 1 KB and
+// a thread's PER_THREAD loads of a round are in flight together (7.0-7.1
+// TB/s where one round per workgroup gave 6.9).  The xor of everything a
+// thread read is stored only if it equals a value that the caller's data does
+// not produce in practice, so the loads stay and nothing is written.
+__global__ __launch_bounds__(SBLOCK) void read16(const u32x4_t *__restrict__ src, size_t n,
+                                                 u32x4_t *__restrict__ sink) {
+    u32x4_t acc = {0u, 0u, 0u, 0u};
+    for (size_t r0 = (size_t)blockIdx.x * ROUND; r0 < n; r0 += (size_t)gridDim.x * ROUND) {
+        const size_t base = r0 + threadIdx.x;
+        u32x4_t v[PER_THREAD];
 #pragma unroll
-    for (int u = 0; u < PER_THREAD; ++u) {
-        const size_t i = base + (size_t)u * BLOCK;
-        v[u] = i < n ? __builtin_nontemporal_load(src + i) : u32x4_t{0u, 0u, 0u, 0u};
+        for (int u = 0; u < PER_THREAD; ++u) {
+            const size_t i = base + (size_t)u * SBLOCK;
+            v[u] = i < n ? __builtin_nontemporal_load(src + i) : u32x4_t{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < PER_THREAD; ++u) acc ^= v[u];
     }
-    u32x4_t acc = v[0];
-#pragma unroll
-    for (int u = 1; u < PER_THREAD; ++u) acc ^= v[u];
     if (acc[0] == 0x9e3779b9u && acc[1] == 0x7f4a7c15u && acc[2] == 0x85ebca6bu &&
         acc[3] == 0xc2b2ae35u)
         sink[0] = acc;
@@ -96,6 +105,13 @@ __global__ __launch_bounds__(BLOCK) void mfma_loop(int iters, f32x4_t *__restric
     if (s == 12345.f) sink[0] = f32x4_t{s, s, s, s};
 }
 
+// two read workgroups per CU, fewer when there are fewer rounds
+unsigned stream_grid(size_t n) {
+    const size_t rounds = (n + ROUND - 1) / ROUND;
+    const size_t g = (size_t)cu_count() * 2;
+    return (unsigned)(rounds < g ? rounds : g);
+}
+
 }  // namespace
 
 extern "C" {
@@ -113,10 +129,9 @@ int beam_peak_copy(const void *src, void *dst, size_t bytes, hipStream_t stream)
 // Reads `bytes` (a multiple of 16) from src; sink: 16 bytes of device memory.
 int beam_peak_read(const void *src, size_t bytes, void *sink, hipStream_t stream) {
     if (!src || !sink || bytes % 16 != 0) return (int)hipErrorInvalidValue;
-    const size_t n = bytes / 16, per = (size_t)BLOCK * PER_THREAD;
+    const size_t n = bytes / 16;
     if (n == 0) return 0;
-    read16<<<(unsigned)((n + per - 1) / per), BLOCK, 0, stream>>>((const u32x4_t *)src, n,
-                                                                  (u32x4_t *)sink);
+    read16<<<stream_grid(n), SBLOCK, 0, stream>>>((const u32x4_t *)src, n, (u32x4_t *)sink);
     return (int)hipGetLastError();
 }
 
