@@ -20,7 +20,7 @@ bf16 MFMA rate, the same kernels with the mask forced all-ones (W_mask = 0,
 plain Top-K), a sweep over the decode batch sizes, the prefill runs (keep
 0.15 / 0.3 / 0.5 / 1.0 at T = 2048 and 8192, and the skewed T = 16384 load),
 a stack of 48 distinct layers at T = 64 under the skewed load (eager and as
-one replayed HIP graph), a DeepSeekV2-Lite-shaped layer with two always-on
+one replayed HIP graph; also at T = 1 and 8), a DeepSeekV2-Lite-shaped layer with two always-on
 shared experts (decode, masked and all-ones), the mask-router backward
 (straight-through estimator + sparsity term), the d=4096/I=1536 layer (decode T = 1 and 64,
 prefill T = 4096, keep 0.15 and 0.5), and the fp64 oracle timed on this
@@ -84,6 +84,8 @@ def parse():
     ap.add_argument("--no-stack", dest="stack", action="store_false")
     ap.add_argument("--stack-T", type=int, default=64)
     ap.add_argument("--stack-steps", type=int, default=20)
+    ap.add_argument("--stack-small", default="1,8",
+                    help="comma list of small T for the same stack (launch-bound decode), '' for none")
     ap.add_argument("--backward", action="store_true", default=True,
                     help="also time the mask-router backward at T = 256, 2048, 8192")
     ap.add_argument("--no-backward", dest="backward", action="store_false")
@@ -427,6 +429,15 @@ def main():
         log(f"stack: {stack['layers']} layers at T={stack['T']}: eager "
             f"{stack['eager']['ms_per_step']:.3f} ms, graph {stack['graph']['ms_per_step']:.3f} ms "
             f"per step")
+    # the same stack at a few tokens, where kernel launches dominate
+    stack_small = []
+    if args.stack and not args.only_headline and args.stack_small:
+        for Ts in (int(v) for v in args.stack_small.split(",") if v):
+            st = run_stack(B, synth, sets, shape, dev, Ts, args.stack_steps, dims=(d, E, K, I))
+            stack_small.append(st)
+            log(f"stack: {st['layers']} layers at T={Ts}: eager "
+                f"{st['eager']['ms_per_step']:.3f} ms, graph {st['graph']['ms_per_step']:.3f} ms "
+                f"per step")
 
     # ---- shared experts: DeepSeekV2-Lite-shaped layer ------------------------
     shared = None
@@ -487,6 +498,7 @@ def main():
         "sweep": sweep_out,
         "prefill": prefill_out,
         "stack": stack,
+        "stack_small": stack_small,
         "shared": shared,
         "mask_backward": backward,
         "large": large,
