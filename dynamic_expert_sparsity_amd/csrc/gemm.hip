@@ -65,6 +65,9 @@ constexpr int G_RPI = 1024 / G_ROWB;  // rows per 1 KB wave load (8)
 #ifndef G_SKIP_A
 #define G_SKIP_A 1
 #endif
+#ifndef G_WN_FAST
+#define G_WN_FAST 1
+#endif
 // the 128-row tiles: rows per wave (32: eight waves, each 32 x 128, half
 // the DMA issues per wave of four 64-row waves; 6-7 us faster down
 // projections at 70-80 pairs per expert) and the k-slices their loads are
@@ -175,7 +178,11 @@ __global__ __launch_bounds__(BM / WT * 128, 1) void grouped_gemm(GemmArgs g) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
-    const int wm = wave % C::WM, wn = wave / C::WM;
+    // column half fastest: consecutive waves sit on different SIMDs (wave w
+    // runs on SIMD w % 4), so the live waves of a part-filled tile (the low
+    // row groups) spread over the SIMDs instead of sharing one
+    const int wn = G_WN_FAST ? wave & 1 : wave / C::WM;
+    const int wm = G_WN_FAST ? wave >> 1 : wave % C::WM;
     const int lr = lane & 31;
     const int lh = lane >> 5;
 
