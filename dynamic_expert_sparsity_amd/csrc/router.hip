@@ -406,6 +406,9 @@ static void launch_select(const Plan &p, const Routing &r, const Work &w, hipStr
 #ifndef BEAM_ROUTER_GEMM_T
 #define BEAM_ROUTER_GEMM_T 8192
 #endif
+#ifndef BEAM_ROUTER_BIG_T
+#define BEAM_ROUTER_BIG_T 2048
+#endif
 #ifndef BEAM_ROUTER_WIDE_T
 #define BEAM_ROUTER_WIDE_T 1024
 #endif
@@ -419,23 +422,30 @@ hipError_t launch_route(const Plan &p, const void *x, const void *Wg, const void
     } else if (p.dtype == 1) {
         // up to a few hundred tokens: 16-token tiles of one column block (the
         // most workgroups, the fewest bytes per workgroup); more: 32-token
-        // tiles; large batches: 64-token tiles of four column blocks, so x and
-        // the weights are each re-read fewer times
-        const int mt = p.T <= BEAM_ROUTER_NARROW_T ? 1 : p.T <= BEAM_ROUTER_WIDE_T ? 2 : 4;
+        // tiles; large batches: tiles of four column blocks, so x and the
+        // weights are each re-read fewer times (32 tokens up to 2048, then 64
+        // tokens with four waves per workgroup, two workgroups per CU)
+        const int mt = p.T <= BEAM_ROUTER_NARROW_T ? 1
+                       : p.T <= BEAM_ROUTER_WIDE_T ? 2 : p.T <= BEAM_ROUTER_BIG_T ? 2 : 4;
         const int ncb = p.T <= BEAM_ROUTER_WIDE_T ? 1 : 4;
         const dim3 grid((p.T + 16 * mt - 1) / (16 * mt), (2 * p.E + 16 * ncb - 1) / (16 * ncb));
 #define BEAM_ROUTER(MTV, NWV, NCV)                                                             \
     router_logits_bf16<MTV, NWV, NCV><<<grid, NWV * 64, 0, s>>>(                              \
         (const bf16_t *)x, (const bf16_t *)Wg, (const bf16_t *)Wm, r.gate_logits,            \
         r.mask_logits, p.T, p.d, p.E)
-        if (p.d % 256 == 0) {
-            if (mt == 1) BEAM_ROUTER(1, 8, 1);
-            else if (mt == 2) BEAM_ROUTER(2, 8, 1);
-            else BEAM_ROUTER(4, 8, 4);
+        // eight waves split d in 256-wide parts (d % 256 == 0), four in d / 4
+        const bool d256 = p.d % 256 == 0;
+        if (mt == 1) {
+            if (d256) BEAM_ROUTER(1, 8, 1);
+            else BEAM_ROUTER(1, 4, 1);
+        } else if (ncb == 1) {
+            if (d256) BEAM_ROUTER(2, 8, 1);
+            else BEAM_ROUTER(2, 4, 1);
+        } else if (mt == 2) {
+            if (d256) BEAM_ROUTER(2, 8, 4);
+            else BEAM_ROUTER(2, 4, 4);
         } else {
-            if (mt == 1) BEAM_ROUTER(1, 4, 1);
-            else if (mt == 2) BEAM_ROUTER(2, 4, 1);
-            else BEAM_ROUTER(4, 4, 4);
+            BEAM_ROUTER(4, 4, 4);
         }
 #undef BEAM_ROUTER
     } else {

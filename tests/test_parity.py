@@ -201,6 +201,15 @@ def test_qwen3_prefill_8192(b):
     _full_check(L, 8, tokens=sample_tokens(8192, 32, seed=2))
 
 
+# the router-logit tilings of large batches with d % 256 != 0 (four waves
+# split d): 32-token tiles of four column blocks (T <= 2048), 64-token tiles
+# above; ragged last tiles and 2E = 16 columns (three of four blocks idle)
+@pytest.mark.parametrize("T", [1500, 3001])
+def test_router_tiles_large_batch(T):
+    L = layer(SMALL, T, seed=1240 + T, mask_bias=0.0)
+    _full_check(L, 2, tokens=sample_tokens(T, 32, seed=6))
+
+
 # above 8192 tokens the logits come from the router GEMM (128-token tiles):
 # last tiles holding 1 and 108 tokens (every logit and route is checked)
 @pytest.mark.parametrize("T", [8193, 8300])
