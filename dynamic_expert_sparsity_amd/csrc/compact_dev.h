@@ -182,6 +182,7 @@ __device__ __forceinline__ void scatter_pair(int p, int K, int TK, int E, int S,
 // expert) its base; wave 0 scans the experts into block-padded offsets; then
 // the block map and pads, and (do_scatter) the position of every pair.  LDS:
 // s_part[nthreads], s_cnt[256], s_off[257].
+template <bool KEEPW>
 __device__ __forceinline__ void scan_tiles(const uint64_t *tile_mask, int n_tiles, int Er, int S,
                                            int bm, int K, int TK, const Routing &r,
                                            int32_t *tile_base, int32_t *pair_pos, int32_t *meta,
@@ -198,9 +199,24 @@ __device__ __forceinline__ void scan_tiles(const uint64_t *tile_mask, int n_tile
     const int tb = g * chunk;
     const int te = min(n_tiles, tb + chunk);
 
+    // KEEPW: up to KEEP tile words per thread stay in registers for the
+    // second pass (worth it for many tiles per thread; with one or two the
+    // re-read is cheaper than the unrolled register copy)
+    constexpr int KEEP = 16;
+    const bool keep = KEEPW && chunk <= KEEP;
+    uint64_t wv[KEEP];
     int local = 0;
-    if (on)
-        for (int t = tb; t < te; ++t) local += __popcll(tile_mask[(size_t)t * E + e]);
+    if (on) {
+        if (keep) {
+#pragma unroll
+            for (int i = 0; i < KEEP; ++i) {
+                wv[i] = tb + i < te ? tile_mask[(size_t)(tb + i) * E + e] : 0ull;
+                local += __popcll(wv[i]);
+            }
+        } else {
+            for (int t = tb; t < te; ++t) local += __popcll(tile_mask[(size_t)t * E + e]);
+        }
+    }
     s_part[tid] = local;
     __syncthreads();
     if (on) {
@@ -210,9 +226,19 @@ __device__ __forceinline__ void scan_tiles(const uint64_t *tile_mask, int n_tile
             if (q < g) base += v;
             total += v;
         }
-        for (int t = tb; t < te; ++t) {
-            tile_base[(size_t)t * E + e] = base;
-            base += __popcll(tile_mask[(size_t)t * E + e]);
+        if (keep) {
+#pragma unroll
+            for (int i = 0; i < KEEP; ++i) {
+                if (tb + i < te) {
+                    tile_base[(size_t)(tb + i) * E + e] = base;
+                    base += __popcll(wv[i]);
+                }
+            }
+        } else {
+            for (int t = tb; t < te; ++t) {
+                tile_base[(size_t)t * E + e] = base;
+                base += __popcll(tile_mask[(size_t)t * E + e]);
+            }
         }
         if (g == 0) s_cnt[e] = total;
     }

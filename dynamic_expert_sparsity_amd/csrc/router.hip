@@ -308,7 +308,9 @@ __global__ __launch_bounds__(256) void select_topk_mask(int T, int E, int S, int
 }
 
 // The grouping of a batch of tiles by one workgroup (and the pair positions
-// when the batch is small).
+// when the batch is small); KEEPW: keep each thread's tile words in registers
+// between the two passes (batches of more than 16 tiles).
+template <bool KEEPW>
 __global__ __launch_bounds__(1024) void compact_tiles(const uint64_t *__restrict__ tile_mask,
                                                       int n_tiles, int E, int S, int bm, int K,
                                                       int TK, Routing r,
@@ -321,8 +323,9 @@ __global__ __launch_bounds__(1024) void compact_tiles(const uint64_t *__restrict
     __shared__ int s_part[1024];
     __shared__ int s_cnt[256];
     __shared__ int s_off[257];
-    scan_tiles(tile_mask, n_tiles, E, S, bm, K, TK, r, tile_base, pair_pos, meta, sorted_tok,
-               pbt, fuse_scatter != 0, split, threadIdx.x, 1024, s_part, s_cnt, s_off);
+    scan_tiles<KEEPW>(tile_mask, n_tiles, E, S, bm, K, TK, r, tile_base, pair_pos, meta,
+                      sorted_tok, pbt, fuse_scatter != 0, split, threadIdx.x, 1024, s_part,
+                      s_cnt, s_off);
 }
 
 // A small batch (T <= 64, one tile) in one workgroup: select, counts,
@@ -384,9 +387,14 @@ static void launch_select_t(const Plan &p, const Routing &r, const Work &w, hipS
     } else {
         select_topk_mask<EJ><<<p.n_tiles * 4, 256, 0, s>>>(p.T, p.E, p.S, p.K, p.thr, r,
                                                           w.tile_mask);
-        compact_tiles<<<1, 1024, 0, s>>>(w.tile_mask, p.n_tiles, p.E, p.S, p.bm, p.K, p.T * p.K,
-                                         r, w.tile_base, w.pair_pos, w.meta, w.sorted_tok, w.pbt,
-                                         p.fuse_scatter, p.split);
+        if (p.n_tiles > 16)
+            compact_tiles<true><<<1, 1024, 0, s>>>(w.tile_mask, p.n_tiles, p.E, p.S, p.bm, p.K,
+                                                   p.T * p.K, r, w.tile_base, w.pair_pos, w.meta,
+                                                   w.sorted_tok, w.pbt, p.fuse_scatter, p.split);
+        else
+            compact_tiles<false><<<1, 1024, 0, s>>>(w.tile_mask, p.n_tiles, p.E, p.S, p.bm, p.K,
+                                                    p.T * p.K, r, w.tile_base, w.pair_pos, w.meta,
+                                                    w.sorted_tok, w.pbt, p.fuse_scatter, p.split);
     }
 }
 
