@@ -44,9 +44,10 @@ def _same(a, b):
 
 
 @pytest.mark.parametrize("shape,Ts", [
-    # small layers: ring kernels (d, I multiples of 256), decode and a batch
-    # large enough for the per-call choice between the two kernel families
-    (synth.LayerShape(512, 32, 4, 256, torch.bfloat16), [1, 64, 64, 700, 33]),
+    # small layers: ring kernels (d, I multiples of 256), decode, a batch
+    # large enough for the per-call choice between the kernel families, and
+    # one of more than 16 select tiles (grouping with separate pair scatter)
+    (synth.LayerShape(512, 32, 4, 256, torch.bfloat16), [1, 64, 64, 700, 33, 3000]),
     # the Qwen3-shaped layer at decode sizes
     ("qwen3", [64, 64, 256]),
 ])
