@@ -12,8 +12,8 @@
 //   d_gate[t, id_j] = g_j (m_j s_j - sum_k g_k m_k s_k)   (softmax over the
 //                     kept logits, Eq. 4, with g_hat = g * m, Eq. 7)
 //
-// Kernels: one wavefront per token for the slot terms (dz, d_gate, and dz
-// transposed in bf16 for the matrix cores); dx as K weighted rows of W_mask
+// Kernels: one wave per token for the slot terms (dz, d_gate, and dz
+// transposed in bf16 for the matrix cores, staged through LDS); dx as K weighted rows of W_mask
 // per token (the K-sparse form of dz W_mask); dW_mask = dz^T x as a bf16 MFMA
 // contraction over the tokens, split over token ranges whose float32
 // partials are then added in a fixed order.
@@ -27,50 +27,69 @@ namespace {
 constexpr int BW_CHUNK = 128;   // tokens per dW k-chunk
 constexpr int BW_LDT = BW_CHUNK + 8;  // LDS row pitch (bf16) of the transposed x chunk
 
-// One wavefront per token t < T_pad (T_pad = T rounded up to BW_CHUNK); lane
-// l owns experts l, l + 64, l + 128, l + 192.  Tokens t >= T only zero their
-// dzT column.
-__global__ __launch_bounds__(256) void mask_bwd_slots(
+constexpr int BS_T = 16;             // tokens per slot-term workgroup (one per wave)
+constexpr int BS_LD = BS_T + 8;      // LDS row pitch (bf16) of the transposed dz group
+
+// A workgroup of 16 waves takes BS_T consecutive tokens, one per wave; lane
+// l owns experts l, l + 64, l + 128, l + 192.  dz and d_gate rows are written
+// as they are made (consecutive lanes, consecutive experts); dz transposed
+// (bf16, for the matrix cores) is collected in LDS as [expert][token of the
+// group] and written out as 32-byte row pieces (two 16-byte stores) instead
+// of one 2-byte store per expert and token.  Tokens t >= T (up to T_pad) only
+// zero their dzT column.
+__global__ __launch_bounds__(1024) void mask_bwd_slots(
     const int32_t *__restrict__ ids, const float *__restrict__ g, const uint8_t *__restrict__ m,
     const float *__restrict__ z, const float *__restrict__ sg, float beta, int T, int T_pad,
     int E, int E_pad, int K, float *__restrict__ dz, float *__restrict__ d_gate,
     bf16_t *__restrict__ dzT) {
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (t >= T_pad) return;
-    float dzv[4] = {0.f, 0.f, 0.f, 0.f}, dgv[4] = {0.f, 0.f, 0.f, 0.f};
-    if (t < T) {
-        const size_t rk = (size_t)t * K;
-        float inner = 0.f;
-        for (int k = 0; k < K; ++k) inner += g[rk + k] * (m[rk + k] ? sg[rk + k] : 0.f);
-        for (int k = 0; k < K; ++k) {
-            const int e = ids[rk + k];
-            const float gk = g[rk + k], sk = sg[rk + k];
-            const float dg = m[rk + k] ? sk : 0.f;
+    __shared__ __align__(16) bf16_t tS[256 * BS_LD];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t0 = blockIdx.x * BS_T;
+    {
+        const int tl = wave;
+        const int t = t0 + tl;
+        float dzv[4] = {0.f, 0.f, 0.f, 0.f}, dgv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (t < T) {
+            const size_t rk = (size_t)t * K;
+            float inner = 0.f;
+            for (int k = 0; k < K; ++k) inner += g[rk + k] * (m[rk + k] ? sg[rk + k] : 0.f);
+            for (int k = 0; k < K; ++k) {
+                const int e = ids[rk + k];
+                const float gk = g[rk + k], sk = sg[rk + k];
+                const float dg = m[rk + k] ? sk : 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (lane + 64 * j == e) {
+                        const float sgm = 1.f / (1.f + expf(-z[(size_t)t * E + e]));
+                        dzv[j] = (gk * sk + beta) * sgm * (1.f - sgm);
+                        dgv[j] = gk * (dg - inner);
+                    }
+                }
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                if (lane + 64 * j == e) {
-                    const float s = 1.f / (1.f + expf(-z[(size_t)t * E + e]));
-                    dzv[j] = (gk * sk + beta) * s * (1.f - s);
-                    dgv[j] = gk * (dg - inner);
+                const int e = lane + 64 * j;
+                if (e < E) {
+                    dz[(size_t)t * E + e] = dzv[j];
+                    if (d_gate) d_gate[(size_t)t * E + e] = dgv[j];
                 }
             }
         }
+        if (dzT) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int e = lane + 64 * j;
-            if (e < E) {
-                dz[(size_t)t * E + e] = dzv[j];
-                if (d_gate) d_gate[(size_t)t * E + e] = dgv[j];
+            for (int j = 0; j < 4; ++j) {
+                const int e = lane + 64 * j;
+                if (e < E_pad) tS[e * BS_LD + tl] = f32_to_bf16(dzv[j]);
             }
         }
     }
-    if (dzT) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int e = lane + 64 * j;
-            if (e < E_pad) dzT[(size_t)e * T_pad + t] = f32_to_bf16(dzv[j]);
-        }
+    if (!dzT) return;
+    __syncthreads();
+    // row e of the group: BS_T tokens = 2 pieces of 16 bytes (t0 + BS_T <= T_pad)
+    for (int q = threadIdx.x; q < E_pad * (BS_T / 8); q += 1024) {
+        const int e = q / (BS_T / 8), c = q - e * (BS_T / 8);
+        *reinterpret_cast<u32x4 *>(dzT + (size_t)e * T_pad + t0 + c * 8) =
+            *reinterpret_cast<const u32x4 *>(&tS[e * BS_LD + c * 8]);
     }
 }
 
@@ -228,7 +247,9 @@ hipError_t launch_mask_backward(const Plan &p, const BwdPlan &b, const void *x, 
     char *wsb = static_cast<char *>(ws);
     bf16_t *dzT = (p.dtype == 1 && dW) ? reinterpret_cast<bf16_t *>(wsb + b.off_dzT) : nullptr;
     const int t_rows = dzT ? b.T_pad : p.T;
-    mask_bwd_slots<<<(t_rows + 3) / 4, 256, 0, s>>>(r.topk_ids, r.topk_weights, r.mask,
+    // with dzT, t_rows = T_pad is a multiple of BW_CHUNK (so of BS_T)
+    static_assert(BW_CHUNK % BS_T == 0, "whole slot groups per dW chunk");
+    mask_bwd_slots<<<(t_rows + BS_T - 1) / BS_T, 1024, 0, s>>>(r.topk_ids, r.topk_weights, r.mask,
                                                     r.mask_logits, sg, beta, p.T, t_rows, p.E,
                                                     b.E_pad, p.K, dz, d_gate, dzT);
     hipError_t err = hipGetLastError();
