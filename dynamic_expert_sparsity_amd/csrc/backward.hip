@@ -154,6 +154,16 @@ __global__ __launch_bounds__(256) void mask_bwd_dw(const bf16_t *__restrict__ dz
 #pragma unroll
     for (int mb = 0; mb < MT; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int t0 = t_begin; t0 < t_end; t0 += BW_CHUNK) {
+        // the chunk's A fragments (dz transposed: 8 consecutive tokens of one
+        // expert per lane) are requested first, so they arrive while x is
+        // staged
+        u32x4 afr[BW_CHUNK / 32][MT];
+#pragma unroll
+        for (int ks = 0; ks < BW_CHUNK / 32; ++ks)
+#pragma unroll
+            for (int mb = 0; mb < MT; ++mb)
+                afr[ks][mb] = ld16(dzT + (size_t)(16 * mb + (lane & 15)) * T_pad + t0 + ks * 32 +
+                                   8 * (lane >> 4));
         // stage x[t0 .. t0+127][c0 .. c0+63]: 4 rows of 8 channels per thread
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -174,10 +184,7 @@ __global__ __launch_bounds__(256) void mask_bwd_dw(const bf16_t *__restrict__ dz
             const u32x4 b = *reinterpret_cast<const u32x4 *>(
                 &xs[(16 * wave + (lane & 15)) * BW_LDT + tk]);
 #pragma unroll
-            for (int mb = 0; mb < MT; ++mb) {
-                const u32x4 a = ld16(dzT + (size_t)(16 * mb + (lane & 15)) * T_pad + t0 + tk);
-                acc[mb] = mfma16x16x32(a, b, acc[mb]);
-            }
+            for (int mb = 0; mb < MT; ++mb) acc[mb] = mfma16x16x32(afr[ks][mb], b, acc[mb]);
         }
         __syncthreads();
     }
