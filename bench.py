@@ -745,7 +745,7 @@ def cpu_baseline(sets, T, K, budget_s):
         total_tok += T
         calls += 1
         del Wgu, Wdt
-        if total_t >= budget_s or calls >= 16:
+        if total_t >= budget_s or calls >= 32:
             break
     log(f"cpu baseline: {calls} layer calls of T={T} in {total_t:.1f}s")
     return {"value": round(total_tok / total_t, 2), "unit": "tok/s", "cores": cores,
