@@ -19,6 +19,12 @@
 
 namespace beam {
 
+// 128-row tiles while they number fewer than BEAM_TILE128_X10 / 10 times the
+// 256-row tiles
+#ifndef BEAM_TILE128_X10
+#define BEAM_TILE128_X10 13
+#endif
+
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -80,7 +86,7 @@ __device__ __forceinline__ void offsets_from_counts(const int *s_cnt, int *s_off
     const int tot_b = __shfl(ib, 63), tot_a = __shfl(ia, 63), tot_q = __shfl(iq, 63);
     const bool tiled = split == 0 || (split != INT_MAX && (2 * tot_b >= 3 * tot_a || mx > 512));
     const int n_bm = __shfl(ip, 63) / bm;
-    const int mode = !tiled ? 0 : (10 * n_bm < 13 * tot_q ? 1 : 2);
+    const int mode = !tiled ? 0 : (10 * n_bm < BEAM_TILE128_X10 * tot_q ? 1 : 2);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int ex = lane * 4 + j;
