@@ -13,7 +13,8 @@ __global__ __launch_bounds__(256) void compact_scatter(Routing r,
                                                       int32_t *__restrict__ sorted_tok) {
     const int p = blockIdx.x * 256 + threadIdx.x;
     if (p >= PT) return;
-    scatter_pair(p, K, TK, E, S, r, r.expert_offsets, tile_base, tile_mask, pair_pos, sorted_tok);
+    scatter_pair(p, p < TK ? r.masked_ids[p] : -1, K, TK, E, S, r, r.expert_offsets, tile_base,
+                 tile_mask, pair_pos, sorted_tok);
 }
 
 hipError_t launch_scatter(const Plan &p, const Routing &r, const Work &w, hipStream_t s) {

@@ -159,13 +159,15 @@ __device__ __forceinline__ void place_pair(int p, int t, int pos, const Routing 
 // Pair p < T*K is routed slot (t, k) = (p / K, p % K); p >= T*K is shared
 // expert E + s of token t, p = T*K + t*S + s.  Tile token sets and bases are
 // [tile][E + S].
-__device__ __forceinline__ void scatter_pair(int p, int K, int TK, int E, int S, const Routing &r,
-                                             const int *off, const int32_t *tile_base,
-                                             const uint64_t *tile_mask, int32_t *pair_pos,
-                                             int32_t *sorted_tok) {
+// mid: the masked id of a routed pair (ignored for shared ones).  The token
+// sets and bases may sit in global memory or in LDS.
+__device__ __forceinline__ void scatter_pair(int p, int mid, int K, int TK, int E, int S,
+                                             const Routing &r, const int *off,
+                                             const int32_t *tile_base, const uint64_t *tile_mask,
+                                             int32_t *pair_pos, int32_t *sorted_tok) {
     int e, t;
     if (p < TK) {
-        e = r.masked_ids[p];
+        e = mid;
         if (e < 0) {
             pair_pos[p] = -1;
             return;
@@ -188,13 +190,20 @@ __device__ __forceinline__ void scatter_pair(int p, int K, int TK, int E, int S,
 // expert) its base; wave 0 scans the experts into block-padded offsets; then
 // the block map and pads, and (do_scatter) the position of every pair.  LDS:
 // s_part[nthreads], s_cnt[256], s_off[257].
-template <bool KEEPW>
+//
+// LOCAL (at most 16 tiles, pairs placed here): the tile words and bases are
+// kept in LDS (s_words, s_tb: [n_tiles][E2]) for the placement, which then
+// reads no global memory but the masked ids, the first PRE of which per
+// thread are requested before anything else.
+template <bool KEEPW, bool LOCAL>
 __device__ __forceinline__ void scan_tiles(const uint64_t *tile_mask, int n_tiles, int Er, int S,
                                            int bm, int K, int TK, const Routing &r,
                                            int32_t *tile_base, int32_t *pair_pos, int32_t *meta,
                                            int32_t *sorted_tok, int32_t *pbt, bool do_scatter,
                                            int split, int tid, int nthreads, int *s_part,
-                                           int *s_cnt, int *s_off) {
+                                           int *s_cnt, int *s_off, uint64_t *s_words,
+                                           int32_t *s_tb) {
+    static_assert(!(KEEPW && LOCAL), "LOCAL is for batches of at most 16 tiles");
     const int E = Er + S;
     const int PT = TK + (TK / K) * S;
     const int NG = nthreads / E;
@@ -204,6 +213,15 @@ __device__ __forceinline__ void scan_tiles(const uint64_t *tile_mask, int n_tile
     const int chunk = (n_tiles + NG - 1) / NG;
     const int tb = g * chunk;
     const int te = min(n_tiles, tb + chunk);
+    constexpr int PRE = 4;  // masked ids requested up front per thread (LOCAL)
+    int mid_pre[PRE];
+    if (LOCAL) {
+#pragma unroll
+        for (int j = 0; j < PRE; ++j) {
+            const int p = tid + j * nthreads;
+            mid_pre[j] = p < TK ? r.masked_ids[p] : -1;
+        }
+    }
 
     // KEEPW: up to KEEP tile words per thread stay in registers for the
     // second pass (worth it for many tiles per thread; with one or two the
@@ -220,7 +238,11 @@ __device__ __forceinline__ void scan_tiles(const uint64_t *tile_mask, int n_tile
                 local += __popcll(wv[i]);
             }
         } else {
-            for (int t = tb; t < te; ++t) local += __popcll(tile_mask[(size_t)t * E + e]);
+            for (int t = tb; t < te; ++t) {
+                const uint64_t w = tile_mask[(size_t)t * E + e];
+                if (LOCAL) s_words[t * E + e] = w;
+                local += __popcll(w);
+            }
         }
     }
     s_part[tid] = local;
@@ -240,6 +262,11 @@ __device__ __forceinline__ void scan_tiles(const uint64_t *tile_mask, int n_tile
                     base += __popcll(wv[i]);
                 }
             }
+        } else if (LOCAL) {
+            for (int t = tb; t < te; ++t) {
+                s_tb[t * E + e] = base;
+                base += __popcll(s_words[t * E + e]);
+            }
         } else {
             for (int t = tb; t < te; ++t) {
                 tile_base[(size_t)t * E + e] = base;
@@ -252,9 +279,26 @@ __device__ __forceinline__ void scan_tiles(const uint64_t *tile_mask, int n_tile
     if (tid < 64) offsets_from_counts(s_cnt, s_off, E, bm, r, meta, pbt, split, tid);
     __syncthreads();
     blocks_and_pads(s_off, s_cnt, E, bm, PT, r, sorted_tok, tid, nthreads);
-    if (do_scatter)
+    if (LOCAL) {
+        // s_words / s_tb were written before the last two barriers
+        for (int j = 0, p = tid; p < PT; ++j, p += nthreads) {
+            int mid = -1;
+            if (p < TK) {
+                if (j >= PRE) {
+                    mid = r.masked_ids[p];
+                } else {
+#pragma unroll
+                    for (int i = 0; i < PRE; ++i)
+                        if (j == i) mid = mid_pre[i];
+                }
+            }
+            scatter_pair(p, mid, K, TK, Er, S, r, s_off, s_tb, s_words, pair_pos, sorted_tok);
+        }
+    } else if (do_scatter) {
         for (int p = tid; p < PT; p += nthreads)
-            scatter_pair(p, K, TK, Er, S, r, s_off, tile_base, tile_mask, pair_pos, sorted_tok);
+            scatter_pair(p, p < TK ? r.masked_ids[p] : -1, K, TK, Er, S, r, s_off, tile_base,
+                         tile_mask, pair_pos, sorted_tok);
+    }
 }
 
 }  // namespace beam

@@ -308,8 +308,10 @@ __global__ __launch_bounds__(256) void select_topk_mask(int T, int E, int S, int
 }
 
 // The grouping of a batch of tiles by one workgroup (and the pair positions
-// when the batch is small); KEEPW: keep each thread's tile words in registers
-// between the two passes (batches of more than 16 tiles).
+// when the batch is small).  KEEPW (batches of more than 16 tiles): keep each
+// thread's tile words in registers between the two passes; the pairs are
+// placed by a separate kernel.  Else (at most 16 tiles, fuse_scatter set):
+// the tile words and bases stay in LDS and the pairs are placed here.
 template <bool KEEPW>
 __global__ __launch_bounds__(1024) void compact_tiles(const uint64_t *__restrict__ tile_mask,
                                                       int n_tiles, int E, int S, int bm, int K,
@@ -323,9 +325,11 @@ __global__ __launch_bounds__(1024) void compact_tiles(const uint64_t *__restrict
     __shared__ int s_part[1024];
     __shared__ int s_cnt[256];
     __shared__ int s_off[257];
-    scan_tiles<KEEPW>(tile_mask, n_tiles, E, S, bm, K, TK, r, tile_base, pair_pos, meta,
-                      sorted_tok, pbt, fuse_scatter != 0, split, threadIdx.x, 1024, s_part,
-                      s_cnt, s_off);
+    __shared__ uint64_t s_words[KEEPW ? 1 : 16 * 256];
+    __shared__ int32_t s_tb[KEEPW ? 1 : 16 * 256];
+    scan_tiles<KEEPW, !KEEPW>(tile_mask, n_tiles, E, S, bm, K, TK, r, tile_base, pair_pos, meta,
+                              sorted_tok, pbt, fuse_scatter != 0, split, threadIdx.x, 1024,
+                              s_part, s_cnt, s_off, s_words, s_tb);
 }
 
 // A small batch (T <= 64, one tile) in one workgroup: select, counts,
@@ -387,7 +391,7 @@ static void launch_select_t(const Plan &p, const Routing &r, const Work &w, hipS
     } else {
         select_topk_mask<EJ><<<p.n_tiles * 4, 256, 0, s>>>(p.T, p.E, p.S, p.K, p.thr, r,
                                                           w.tile_mask);
-        if (p.n_tiles > 16)
+        if (!p.fuse_scatter)  // more than 16 tiles
             compact_tiles<true><<<1, 1024, 0, s>>>(w.tile_mask, p.n_tiles, p.E, p.S, p.bm, p.K,
                                                    p.T * p.K, r, w.tile_base, w.pair_pos, w.meta,
                                                    w.sorted_tok, w.pbt, p.fuse_scatter, p.split);
