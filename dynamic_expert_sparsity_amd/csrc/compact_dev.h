@@ -25,12 +25,21 @@ namespace beam {
 #define BEAM_TILE128_X10 13
 #endif
 
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(v, off);
-        if (lane >= off) v += y;
-    }
+// Inclusive prefix sum over the 64 lanes with DPP moves (no LDS round
+// trips): shifts by 1, 2, 4, 8 within each row of 16 lanes (lanes without a
+// source add 0), then row 15's total added to rows 1 and 3 and lane 31's to
+// rows 2 and 3.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_add(int v) {
+    return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xF, false);
+}
+__device__ __forceinline__ int wave_incl_scan(int v, int /*lane*/) {
+    v = dpp_add<0x111, 0xF>(v);  // row_shr:1
+    v = dpp_add<0x112, 0xF>(v);  // row_shr:2
+    v = dpp_add<0x114, 0xF>(v);  // row_shr:4
+    v = dpp_add<0x118, 0xF>(v);  // row_shr:8
+    v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
+    v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
     return v;
 }
 
