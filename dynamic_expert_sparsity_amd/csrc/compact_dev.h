@@ -74,8 +74,13 @@ __device__ __forceinline__ void offsets_from_counts(const int *s_cnt, int *s_off
         sb += npb[j];
         mx = max(mx, c[j]);
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o));
+    // largest count: within each row of 16 by DPP, then the four rows' maxima
+    mx = max(mx, __builtin_amdgcn_update_dpp(0, mx, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    mx = max(mx, __builtin_amdgcn_update_dpp(0, mx, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    mx = max(mx, __builtin_amdgcn_update_dpp(0, mx, 0x141, 0xF, 0xF, false));  // row_half_mirror
+    mx = max(mx, __builtin_amdgcn_update_dpp(0, mx, 0x140, 0xF, 0xF, false));  // row_mirror
+    mx = max(max(__builtin_amdgcn_readlane(mx, 0), __builtin_amdgcn_readlane(mx, 16)),
+             max(__builtin_amdgcn_readlane(mx, 32), __builtin_amdgcn_readlane(mx, 48)));
     const int ic = wave_incl_scan(sc, lane);
     const int ip = wave_incl_scan(sp, lane);
     const int ia = wave_incl_scan(sa, lane);
@@ -92,9 +97,10 @@ __device__ __forceinline__ void offsets_from_counts(const int *s_cnt, int *s_off
     // count stays under 1.3 x the 256-row tiles' (measured on the Qwen3-shaped
     // layer: 128-row tiles are 13-15% faster at ratios near 1, 256-row tiles
     // about 4% faster at ratios near 1.5)
-    const int tot_b = __shfl(ib, 63), tot_a = __shfl(ia, 63), tot_q = __shfl(iq, 63);
+    const int tot_b = __builtin_amdgcn_readlane(ib, 63), tot_a = __builtin_amdgcn_readlane(ia, 63),
+              tot_q = __builtin_amdgcn_readlane(iq, 63);
     const bool tiled = split == 0 || (split != INT_MAX && (2 * tot_b >= 3 * tot_a || mx > 512));
-    const int n_bm = __shfl(ip, 63) / bm;
+    const int n_bm = __builtin_amdgcn_readlane(ip, 63) / bm;
     const int mode = !tiled ? 0 : (10 * n_bm < BEAM_TILE128_X10 * tot_q ? 1 : 2);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
