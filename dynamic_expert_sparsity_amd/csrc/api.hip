@@ -92,6 +92,14 @@ int make_plan(const beam_moe_desc *desc, Plan &p) {
     p.n_tiles = (D.T + 63) / 64;
     p.fuse_scatter = p.n_tiles <= 16;
     p.max_active = (int)(PT < p.E2 ? PT : p.E2);
+    // the streaming kernels number their units (position blocks of <= 32 x
+    // column groups of 16 units up / 32 channels down) in int
+    if (D.dtype == BEAM_BF16) {
+        const long long blocks = (long long)p.max_active + PT / 32 + 1;
+        const long long groups = D.I / 16 > D.d / 32 ? D.I / 16 : D.d / 32;
+        if (blocks * groups >= (1ll << 31))
+            return fail(BEAM_EUNSUPPORTED, "T=%d is too large for the streaming kernels", D.T);
+    }
     const long long cap_raw = PT + (long long)p.max_active * (p.bm - 1);
     p.cap = (cap_raw + p.bm - 1) / p.bm * p.bm;
     p.n_blocks_cap = p.cap / p.bm;

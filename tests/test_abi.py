@@ -88,6 +88,8 @@ def test_query_sizes(T, d, E, K, I, dt):
     (dict(I=128, flags=2, block_m=256), B.BEAM_EUNSUPPORTED),
     (dict(I=128, flags=2, block_m=64), B.BEAM_EUNSUPPORTED),
     (dict(I=64, flags=2), B.BEAM_EUNSUPPORTED),
+    # the streaming kernels' unit count must fit an int
+    (dict(T=40_000_000, d=8192, E=128, K=8, I=768), B.BEAM_EUNSUPPORTED),
 ])
 def test_query_rejects(kw, code):
     a = dict(T=4, d=256, E=16, K=2, I=64, dtype=1, block_m=0, flags=0, tau=0.0)
