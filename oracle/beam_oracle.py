@@ -18,7 +18,7 @@ Everything here is plain, slow and obviously correct:
   * one library primitive per step (a matmul, a lexsort), no blocking, no
     fusion, no reordering beyond what the equations state.
 
-Readings of points the pages leave open (each is also listed in the design doc):
+Readings of points the pages leave open:
   R1  no router biases: r = x W_gate^T, z = x W_mask^T (weights stored
       [E, d], one row per expert, i.e. the transpose of the paper's
       W_m in R^{d_h x N});
