@@ -89,8 +89,12 @@ __device__ __forceinline__ void offsets_from_counts(const int *s_cnt, int *s_off
     int op = ip - sp, oa = ia - sa, ob = ib - sb, oq = iq - sq;
     // expert kernels for this call (Plan::split).  The streaming kernels
     // stream an expert's weights once per block of 32 positions: the tiled
-    // kernels take the call once those re-reads reach half the active
-    // experts' weights, or one expert has more than 512 pairs.  A tiled tile
+    // kernels take the call once those re-reads reach a quarter of the
+    // active experts' weights, or one expert has more than 512 pairs
+    // (measured on the Qwen3-shaped layer at 1024-2048 tokens: the streaming
+    // kernels' time grows with the blocks per active expert, ~264 us per
+    // layer at 1.0, while the tiled kernels' stays near 320 us; they cross
+    // near 1.2).  A tiled tile
     // reads its expert's weight slice once and computes all its rows: 128-row
     // tiles waste fewer rows on sparse experts, 256-row tiles read the weights
     // of a dense expert half as often; 128-row tiles are taken while their
@@ -99,7 +103,7 @@ __device__ __forceinline__ void offsets_from_counts(const int *s_cnt, int *s_off
     // about 4% faster at ratios near 1.5)
     const int tot_b = __builtin_amdgcn_readlane(ib, 63), tot_a = __builtin_amdgcn_readlane(ia, 63),
               tot_q = __builtin_amdgcn_readlane(iq, 63);
-    const bool tiled = split == 0 || (split != INT_MAX && (2 * tot_b >= 3 * tot_a || mx > 512));
+    const bool tiled = split == 0 || (split != INT_MAX && (4 * tot_b >= 5 * tot_a || mx > 512));
     const int n_bm = __builtin_amdgcn_readlane(ip, 63) / bm;
     const int mode = !tiled ? 0 : (10 * n_bm < BEAM_TILE128_X10 * tot_q ? 1 : 2);
 #pragma unroll

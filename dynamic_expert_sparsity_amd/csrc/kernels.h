@@ -18,7 +18,7 @@ struct Plan {
     int path;           // 0 streaming (decode), 1 tiled (prefill)
     int split;          // INT_MAX: streaming kernels only; 0: tiled kernels only;
                         // else (1) chosen per call on the device: tiled if the
-                        // blocks of <= 32 positions number >= 1.5 x the active
+                        // blocks of <= 32 positions number >= 1.25 x the active
                         // experts or one expert has more than 512 pairs (the
                         // per-call record meta)
     float thr;          // mask logit threshold: m = [z >= thr]

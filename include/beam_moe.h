@@ -68,7 +68,7 @@ extern "C" {
                                          T > 512, the device picks per call from
                                          the routed counts: tiled kernels if the
                                          blocks of <= 32 positions per expert
-                                         number >= 1.5 x the active experts, or
+                                         number >= 1.25 x the active experts, or
                                          one expert has > 512 active pairs, else
                                          the streaming kernels.  Tiled calls use
                                          128-row tiles while those number < 1.3 x

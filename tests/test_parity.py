@@ -128,16 +128,16 @@ def test_prefill_and_decode_paths_agree():
 
 
 # ---- default above 512 tokens: the device picks, per call, the tiled kernels
-# (blocks of <= 32 positions number >= 1.5 x the active experts, or one expert
-# above 512 pairs) or the streaming kernels; skewed routing at E=16 lands on
-# the tiled side, at E=32 on the streaming side
+# (blocks of <= 32 positions number >= 1.25 x the active experts, or one
+# expert above 512 pairs) or the streaming kernels; skewed routing at E=16
+# lands on the tiled side, at E=96 on the streaming side
 def _expects_tiled(counts):
     act = counts[counts > 0]
     blocks = ((act + 31) // 32).sum()
-    return 2 * blocks >= 3 * len(act) or counts.max() > 512
+    return 4 * blocks >= 5 * len(act) or counts.max() > 512
 
 
-@pytest.mark.parametrize("E,tiled", [(16, True), (32, False)])
+@pytest.mark.parametrize("E,tiled", [(16, True), (96, False)])
 def test_per_call_kernel_choice(E, tiled):
     import dynamic_expert_sparsity_amd as B
     shape = synth.LayerShape(256, E, 2, 128, torch.bfloat16)
@@ -162,7 +162,7 @@ def _mode_record(lay):
 
 def _expected_family(counts, forced):
     act = counts[counts > 0]
-    tiled = forced or 2 * ((act + 31) // 32).sum() >= 3 * len(act) or counts.max() > 512
+    tiled = forced or 4 * ((act + 31) // 32).sum() >= 5 * len(act) or counts.max() > 512
     if not tiled:
         return 0
     n128 = ((act + 127) // 128).sum()
@@ -193,6 +193,23 @@ def test_kernel_family_choice(T, forced, b, family):
     assert rec[0] == family, "the inputs did not land on the intended family"
     if family == 2:
         assert rec[2] == ((counts[counts > 0] + 255) // 256).sum()
+
+
+# ---- the streaming kernels on the tiled path (two column groups per unit,
+# ranges that begin or end with half a unit), with a short last k-chunk in
+# the down projection (I = 384 ends in 128 of a 256-chunk; the tiled path
+# needs d % 256 == 0, so the up projection has none there)
+@pytest.mark.parametrize("T", [700, 1500])
+def test_streaming_on_tiled_path_short_chunks(T):
+    import dynamic_expert_sparsity_amd as B
+    shape = synth.LayerShape(512, 64, 4, 384, torch.bfloat16)
+    L = layer(shape, T, seed=1600 + T, mask_bias=-1.5)
+    y, G, O, _ = _full_check(L, 4, tokens=sample_tokens(T, 256, seed=T))
+    lay = B.MoELayer(L["W_gate"], L["W_mask"], L["W_gu"], L["W_dt"], 4)
+    lay(L["x"])
+    torch.cuda.synchronize()
+    assert lay.sizes["path"] == 1
+    assert _mode_record(lay)[0] == _expected_family(G["counts"], False) == 0
 
 
 @pytest.mark.parametrize("b", [0.0, 8.0])
