@@ -235,7 +235,9 @@ def test_router_gemm_ragged(T):
     _full_check(L, 2, tokens=sample_tokens(T, 32, seed=5))
 
 
-@pytest.mark.parametrize("T,b", [(1, -1.04), (64, 0.0), (4096, -1.04)])
+# (T = 1024 at keep 0.15: the streaming kernels on the tiled path; T = 4096:
+# the tiled kernels)
+@pytest.mark.parametrize("T,b", [(1, -1.04), (64, 0.0), (1024, -1.04), (4096, -1.04)])
 def test_large_layer(T, b):
     L = layer("large", T, seed=1300 + T, mask_bias=b)
     _full_check(L, 8, tokens=sample_tokens(T, 24, seed=4))
