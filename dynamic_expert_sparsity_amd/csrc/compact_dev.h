@@ -47,7 +47,7 @@ __device__ __forceinline__ int wave_incl_scan(int v, int /*lane*/) {
 // (E <= 256, four experts per lane) write block-padded exclusive offsets to
 // s_off[0..E] and r.expert_offsets, the ascending active-expert list and
 // r.num_active = {P, num_padded, n_active_experts, n_blocks}, the call's
-// record meta = {kernel family, max count, records, 0} and the work records
+// record meta = {kernel family, max count, records, layout} and the work records
 // of the family (pbt, in expert order): the streaming kernels (family 0) get
 // one record {expert, first position, rows, 0} per block of up to 32
 // consecutive positions of an expert; the 256-row tiled kernels (family 2)
@@ -136,7 +136,13 @@ __device__ __forceinline__ void offsets_from_counts(const int *s_cnt, int *s_off
         r.num_active[1] = ip;
         r.num_active[2] = ia;
         r.num_active[3] = ip / bm;
-        *reinterpret_cast<int4 *>(meta) = make_int4(mode, mx, mode == 2 ? iq : ib, 0);
+        // streaming kernels' layout: two column groups per unit once the
+        // blocks of 32 positions hold 6 routed pairs or more on average (their
+        // x rows then cost about as much as the weights; measured on the
+        // Qwen3-shaped layer: one group is faster at ~2.6 and ~4.8 pairs per
+        // block, two at ~7 and above)
+        const int wide = ic >= 6 * ib ? 1 : 0;
+        *reinterpret_cast<int4 *>(meta) = make_int4(mode, mx, mode == 2 ? iq : ib, wide);
     }
 }
 

@@ -189,7 +189,7 @@ __device__ __forceinline__ void ring_dma(const void *g, unsigned char *l) {
 // one per output channel of a column group of 32; out o).  klen = d (up) or
 // I (down), a multiple of 64; ncols = I (up) or d (down).
 template <bool DOWN, bool TAIL>
-__global__ __launch_bounds__(512, 1) void ring_bf16(
+__device__ __forceinline__ void ring1_body(
     const bf16_t *__restrict__ A, const bf16_t *__restrict__ W,
     const int32_t *__restrict__ pbt, const int32_t *__restrict__ mrec,
     const int32_t *__restrict__ sorted_tok, bf16_t *__restrict__ out, int klen, int ncols,
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(512, 1) void ring_bf16(
     constexpr int NS = RING_NS;
     extern __shared__ __align__(16) unsigned char lds[];
     f32x4 *red = reinterpret_cast<f32x4 *>(lds + NS * RING_SLOT);  // [wave][2 col blocks x 2 row blocks][lane]
-    // mrec = {kernel family, max count, records, 0}; family 1 or 2: the tiled kernels take this call
+    // mrec = {kernel family, max count, records, layout}; family 1 or 2: the tiled kernels take this call
     if (check_mode && mrec[0] != 0) return;
     const int NCH = (klen + 255) >> 8;             // k-chunks of 256 per row (last may be short)
     // elements of a short last chunk (TAIL instances only; else klen % 256 == 0)
@@ -377,10 +377,12 @@ __global__ __launch_bounds__(512, 1) void ring_bf16(
 }
 
 // ---------------------------------------------------------------------------
-// The same projections on the tiled path (more than 512 tokens, when the
-// per-call choice keeps the streaming kernels), where blocks hold more
-// positions and the x loads of the ring above would cost as much as its
-// weight loads.  A unit is (block of up to 32 positions, pair of column
+// The same projections with two column groups per unit, taken per call when
+// the blocks hold more positions (the compaction's layout flag: at least 6
+// routed pairs per block of 32 on average), where the x loads of the ring
+// above cost about as much as its weight loads: its x rows are then mostly
+// distinct tokens, and with more than 16 positions a block needs two x
+// loads per chunk.  A unit is (block of up to 32 positions, pair of column
 // groups): 64 weight rows, so each k-chunk of the block's x rows serves 64
 // weight rows.  The work is still split over the grid in column groups (half
 // units), so a workgroup's range may begin or end with half a unit.  A slot
@@ -410,17 +412,17 @@ __device__ __forceinline__ void ring2_wait_le(int n) {
     else if (n >= 1) ring_wait_vm<1>();
     else ring_wait_vm<0>();
 }
-// DOWN as for ring_bf16; ncols = I (up, a multiple of 32) or d (down, a
+// DOWN as for ring1_body; ncols = I (up, a multiple of 32) or d (down, a
 // multiple of 64).
 template <bool DOWN, bool TAIL>
-__global__ __launch_bounds__(512, 1) void ring2_bf16(
+__device__ __forceinline__ void ring2_body(
     const bf16_t *__restrict__ A, const bf16_t *__restrict__ W,
     const int32_t *__restrict__ pbt, const int32_t *__restrict__ mrec,
     const int32_t *__restrict__ sorted_tok, bf16_t *__restrict__ out, int klen, int ncols,
     int check_mode) {
     constexpr int NS = RING2_NS;
     extern __shared__ __align__(16) unsigned char lds[];
-    // mrec = {kernel family, max count, records, 0}; family 1 or 2: the tiled kernels take this call
+    // mrec = {kernel family, max count, records, layout}; family 1 or 2: the tiled kernels take this call
     if (check_mode && mrec[0] != 0) return;
     const int NCH = (klen + 255) >> 8;             // k-chunks of 256 per row (last may be short)
     // elements of a short last chunk (TAIL instances only; else klen % 256 == 0)
@@ -629,9 +631,24 @@ __global__ __launch_bounds__(512, 1) void ring2_bf16(
 }
 
 
+// The streaming kernel: the per-call record's layout flag (mrec[3], set by
+// the compaction when the routed pairs number at least 6 per block of 32
+// positions) picks two column groups per unit, else one.
+template <bool DOWN, bool TAIL>
+__global__ __launch_bounds__(512, 1) void ring_bf16(
+    const bf16_t *__restrict__ A, const bf16_t *__restrict__ W,
+    const int32_t *__restrict__ pbt, const int32_t *__restrict__ mrec,
+    const int32_t *__restrict__ sorted_tok, bf16_t *__restrict__ out, int klen, int ncols,
+    int check_mode) {
+    if (mrec[3])
+        ring2_body<DOWN, TAIL>(A, W, pbt, mrec, sorted_tok, out, klen, ncols, check_mode);
+    else
+        ring1_body<DOWN, TAIL>(A, W, pbt, mrec, sorted_tok, out, klen, ncols, check_mode);
+}
+
 // The ring kernels need a k length (d for up, I for down) that is a multiple
-// of 64 and whole units (I % 32 for up, d % 64 for down, as ring2_bf16
-// needs): the descriptor checks of a bf16 layer (d % 128 == 0, I % 64 == 0)
+// of 64 and whole units (I % 32 for up, d % 64 for down, as the
+// two-column-group layout needs): the descriptor checks of a bf16 layer (d % 128 == 0, I % 64 == 0)
 // imply both.
 static int ring_grid() {
     static int n = 0;
@@ -659,21 +676,16 @@ static hipError_t ring_attr(const void *fn, int bytes) {
     return hipSuccess;
 }
 
-// one ring launch (ring2_bf16 on the tiled path); TAIL: the k length ends in a short chunk
+// one ring launch; TAIL: the k length ends in a short chunk
 template <bool DOWN, bool TAIL>
 static hipError_t launch_ring_t(const void *A, const void *W, const Plan &p, const Work &w, void *out,
                                 int klen, int ncols, hipStream_t s) {
-    const bool wide = p.path == 1;
-    const void *fn = wide ? (const void *)ring2_bf16<DOWN, TAIL> : (const void *)ring_bf16<DOWN, TAIL>;
-    const int lds = wide ? RING2_LDS : RING_LDS;
-    const hipError_t e = ring_attr(fn, lds);
+    static_assert(RING2_LDS <= RING_LDS, "one LDS size for both layouts");
+    const hipError_t e = ring_attr((const void *)ring_bf16<DOWN, TAIL>, RING_LDS);
     if (e != hipSuccess) return e;
-    if (wide)
-        ring2_bf16<DOWN, TAIL><<<ring_grid(), 512, lds, s>>>(
-            (const bf16_t *)A, (const bf16_t *)W, w.pbt, w.meta, w.sorted_tok, (bf16_t *)out, klen, ncols, 1);
-    else
-        ring_bf16<DOWN, TAIL><<<ring_grid(), 512, lds, s>>>(
-            (const bf16_t *)A, (const bf16_t *)W, w.pbt, w.meta, w.sorted_tok, (bf16_t *)out, klen, ncols, 0);
+    ring_bf16<DOWN, TAIL><<<ring_grid(), 512, RING_LDS, s>>>(
+        (const bf16_t *)A, (const bf16_t *)W, w.pbt, w.meta, w.sorted_tok, (bf16_t *)out, klen, ncols,
+        p.path == 1 ? 1 : 0);
     return hipGetLastError();
 }
 template <bool DOWN>

@@ -150,7 +150,7 @@ def test_per_call_kernel_choice(E, tiled):
 
 
 def _mode_record(lay):
-    """The call's kernel-family record {family, max count, records, 0} from
+    """The call's kernel-family record {family, max count, records, layout} from
     the workspace (layout: tile token sets, tile bases, pair positions, then
     the record, each piece rounded up to 256 bytes)."""
     al = lambda v: (v + 255) // 256 * 256  # noqa: E731
@@ -210,6 +210,27 @@ def test_streaming_on_tiled_path_short_chunks(T):
     torch.cuda.synchronize()
     assert lay.sizes["path"] == 1
     assert _mode_record(lay)[0] == _expected_family(G["counts"], False) == 0
+
+
+# ---- the streaming kernels' layout, chosen per call on the device: two
+# column groups per unit once the routed pairs number >= 6 per block of <= 32
+# positions (T = 500 keep ~0.5: ~16 pairs per expert), else one (keep ~0.15:
+# ~5); on the streaming path (T <= 512) and forced decode above it
+@pytest.mark.parametrize("T,b,flags,wide", [(500, 0.0, 0, 1), (500, -1.04, 0, 0),
+                                            (1200, 0.0, 1, 1), (200, 8.0, 0, 1)])
+def test_streaming_layout_choice(T, b, flags, wide):
+    import dynamic_expert_sparsity_amd as B
+    L = layer("qwen3", T, seed=1700 + T, mask_bias=b)
+    y, G, O, _ = _full_check(L, 8, flags=flags, tokens=sample_tokens(T, 24, seed=T))
+    lay = B.MoELayer(L["W_gate"], L["W_mask"], L["W_gu"], L["W_dt"], 8, flags=flags)
+    lay(L["x"])
+    torch.cuda.synchronize()
+    assert lay.sizes["path"] == 0
+    counts = G["counts"]
+    blocks = ((counts[counts > 0] + 31) // 32).sum()
+    rec = _mode_record(lay)
+    assert rec[0] == 0 and rec[2] == blocks
+    assert rec[3] == (1 if counts.sum() >= 6 * blocks else 0) == wide
 
 
 @pytest.mark.parametrize("b", [0.0, 8.0])
