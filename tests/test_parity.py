@@ -233,6 +233,23 @@ def test_streaming_layout_choice(T, b, flags, wide):
     assert rec[3] == (1 if counts.sum() >= 6 * blocks else 0) == wide
 
 
+# ---- both streaming layouts with short last k-chunks in both projections
+# (d = 384 and I = 320 end in 128 and 64 of a 256-chunk)
+@pytest.mark.parametrize("T,b,wide", [(300, 8.0, 1), (300, -1.5, 0), (37, 8.0, 1)])
+def test_streaming_layouts_short_chunks(T, b, wide):
+    import dynamic_expert_sparsity_amd as B
+    shape = synth.LayerShape(384, 16, 4, 320, torch.bfloat16)
+    L = layer(shape, T, seed=1800 + T, mask_bias=b)
+    y, G, O, _ = _full_check(L, 4, tokens=sample_tokens(T, 64, seed=T))
+    lay = B.MoELayer(L["W_gate"], L["W_mask"], L["W_gu"], L["W_dt"], 4)
+    lay(L["x"])
+    torch.cuda.synchronize()
+    assert lay.sizes["path"] == 0
+    counts = G["counts"]
+    blocks = ((counts[counts > 0] + 31) // 32).sum()
+    assert _mode_record(lay)[3] == (1 if counts.sum() >= 6 * blocks else 0) == wide
+
+
 @pytest.mark.parametrize("b", [0.0, 8.0])
 def test_qwen3_prefill_8192(b):
     L = layer("qwen3", 8192, seed=1200, mask_bias=b)
