@@ -341,15 +341,18 @@ class RoutingStats:
             t.zero_()
 
 
-def route(x, W_gate, W_mask, K, block_m=0, flags=0, tau=0.0, stream=None, n_shared=0) -> dict:
+def route(x, W_gate, W_mask, K, I, block_m=0, flags=0, tau=0.0, stream=None, n_shared=0) -> dict:
     """beam_moe_route: routing tensors for x (new buffers); the grouping
-    includes n_shared always-on experts numbered E .. E+n_shared-1."""
+    includes n_shared always-on experts numbered E .. E+n_shared-1.  I is the
+    layer's intermediate size: with the other sizes it fixes the expert
+    kernels' path and block size, so the lists come out padded exactly as
+    beam_moe_forward pads them for the same layer."""
     E, d = W_gate.shape
     _gpu_tensor("x", x, W_gate.dtype)
     _gpu_tensor("W_gate", W_gate, x.dtype, (E, d))
     _gpu_tensor("W_mask", W_mask, x.dtype, (E, d))
     T = x.shape[0]
-    desc = make_desc(T, d, E, K, 64, x.dtype, block_m, flags, tau, n_shared)  # I unused by routing
+    desc = make_desc(T, d, E, K, I, x.dtype, block_m, flags, tau, n_shared)
     sizes = query(desc)
     R = alloc_routing(desc, sizes, x.device)
     ws = torch.empty(max(sizes["route_workspace_bytes"], 256), dtype=torch.uint8, device=x.device)
@@ -357,6 +360,7 @@ def route(x, W_gate, W_mask, K, block_m=0, flags=0, tau=0.0, stream=None, n_shar
                                 W_mask.data_ptr(), ctypes.byref(_routing_struct(R)),
                                 ws.data_ptr(), ws.numel(), _stream_ptr(stream)))
     R["_ws"] = ws  # keep alive until the stream has used it
+    R["_sizes"] = sizes
     return R
 
 

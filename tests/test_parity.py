@@ -5,7 +5,9 @@ relative L2); every discrete routing output (ids, mask bits, -1 ids, counts,
 offsets, sorted lists, block map, active list) bit-exact against the oracle
 run on the GPU's own float32 logits; y within relative L2 1e-2 (bf16 layer)
 or 1e-5 (float32 layer) of the oracle's Eq. 8 on the same routing; tokens
-with every slot masked exactly 0.
+with every slot masked exactly 0.  The y bound holds for the checked rows
+together and for each row alone; unless a test names a sample, every row is
+checked.
 """
 import numpy as np
 import pytest
@@ -14,7 +16,7 @@ import torch
 import oracle
 from dynamic_expert_sparsity_amd import synth
 from beamtest import (check_logits, check_routing_exact, check_y, gpu_routing_host, host, layer,
-                      need_gpu, run, sample_tokens)
+                      mode_record, need_gpu, run, sample_tokens)
 
 pytestmark = pytest.mark.gpu
 
@@ -84,7 +86,7 @@ def test_threshold_variants(tau):
 @pytest.mark.parametrize("mode", ["bias", "zero"])
 def test_qwen3_decode(T, mode):
     L = layer("qwen3", T, seed=600 + T, mask_bias=-1.04, mask_mode=mode)
-    _full_check(L, 8, tokens=sample_tokens(T, 48, seed=T))
+    _full_check(L, 8)
 
 
 @pytest.mark.parametrize("b", [-1.04, 8.0])
@@ -149,17 +151,6 @@ def test_per_call_kernel_choice(E, tiled):
     assert lay.sizes["path"] == 1 and lay.sizes["block_m"] == 128
 
 
-def _mode_record(lay):
-    """The call's kernel-family record {family, max count, records, layout} from
-    the workspace (layout: tile token sets, tile bases, pair positions, then
-    the record, each piece rounded up to 256 bytes)."""
-    al = lambda v: (v + 255) // 256 * 256  # noqa: E731
-    T, E2, K, S = lay.desc.T, lay.desc.E + lay.desc.n_shared, lay.desc.K, lay.desc.n_shared
-    n_tiles = (T + 63) // 64
-    off = al(n_tiles * E2 * 8) + al(n_tiles * E2 * 4) + al(T * (K + S) * 4)
-    return lay.ws[off:off + 16].view(torch.int32).cpu().numpy()
-
-
 def _expected_family(counts, forced):
     act = counts[counts > 0]
     tiled = forced or 4 * ((act + 31) // 32).sum() >= 5 * len(act) or counts.max() > 512
@@ -183,11 +174,11 @@ def test_kernel_family_choice(T, forced, b, family):
     shape = synth.LayerShape(256, 16, 4, 128, torch.bfloat16)
     flags = B.BEAM_FORCE_PREFILL if forced else 0
     L = layer(shape, T, seed=1400 + T, mask_bias=b)
-    y, G, O, _ = _full_check(L, 4, flags=flags, tokens=sample_tokens(T, 256, seed=T))
+    y, G, O, _ = _full_check(L, 4, flags=flags)
     lay = B.MoELayer(L["W_gate"], L["W_mask"], L["W_gu"], L["W_dt"], 4, flags=flags)
     lay(L["x"])
     torch.cuda.synchronize()
-    rec = _mode_record(lay)
+    rec = mode_record(lay)
     counts = G["counts"]
     assert rec[0] == _expected_family(counts, forced)
     assert rec[0] == family, "the inputs did not land on the intended family"
@@ -195,21 +186,29 @@ def test_kernel_family_choice(T, forced, b, family):
         assert rec[2] == ((counts[counts > 0] + 255) // 256).sum()
 
 
-# ---- the streaming kernels on the tiled path (two column groups per unit,
-# ranges that begin or end with half a unit), with a short last k-chunk in
-# the down projection (I = 384 ends in 128 of a 256-chunk; the tiled path
-# needs d % 256 == 0, so the up projection has none there)
-@pytest.mark.parametrize("T", [700, 1500])
-def test_streaming_on_tiled_path_short_chunks(T):
+# ---- the streaming kernels on the tiled path (above 512 tokens, where the
+# device may still pick them), in both layouts: one column group per unit
+# (~3 routed pairs per block of <= 32 positions at T = 700, b = -1.5) and two
+# (~20 pairs per block at b = -0.1, whose ranges may begin or end with half a
+# unit); the down projection's k length I = 384 ends in a short chunk (128
+# of 256; the tiled path needs d % 256 == 0, so the up projection has none)
+@pytest.mark.parametrize("T,b,wide", [(700, -1.5, 0), (700, -0.1, 1), (1500, -1.5, None)])
+def test_streaming_on_tiled_path_short_chunks(T, b, wide):
     import dynamic_expert_sparsity_amd as B
     shape = synth.LayerShape(512, 64, 4, 384, torch.bfloat16)
-    L = layer(shape, T, seed=1600 + T, mask_bias=-1.5)
-    y, G, O, _ = _full_check(L, 4, tokens=sample_tokens(T, 256, seed=T))
+    L = layer(shape, T, seed=1600 + T, mask_bias=b)
+    y, G, O, _ = _full_check(L, 4)
     lay = B.MoELayer(L["W_gate"], L["W_mask"], L["W_gu"], L["W_dt"], 4)
     lay(L["x"])
     torch.cuda.synchronize()
     assert lay.sizes["path"] == 1
-    assert _mode_record(lay)[0] == _expected_family(G["counts"], False) == 0
+    rec = mode_record(lay)
+    counts = G["counts"]
+    assert rec[0] == _expected_family(counts, False) == 0
+    blocks = ((counts[counts > 0] + 31) // 32).sum()
+    assert rec[3] == (1 if counts.sum() >= 6 * blocks else 0)
+    if wide is not None:
+        assert rec[3] == wide, "the inputs did not land on the intended layout"
 
 
 # ---- the streaming kernels' layout, chosen per call on the device: two
@@ -221,14 +220,14 @@ def test_streaming_on_tiled_path_short_chunks(T):
 def test_streaming_layout_choice(T, b, flags, wide):
     import dynamic_expert_sparsity_amd as B
     L = layer("qwen3", T, seed=1700 + T, mask_bias=b)
-    y, G, O, _ = _full_check(L, 8, flags=flags, tokens=sample_tokens(T, 24, seed=T))
+    y, G, O, _ = _full_check(L, 8, flags=flags)
     lay = B.MoELayer(L["W_gate"], L["W_mask"], L["W_gu"], L["W_dt"], 8, flags=flags)
     lay(L["x"])
     torch.cuda.synchronize()
     assert lay.sizes["path"] == 0
     counts = G["counts"]
     blocks = ((counts[counts > 0] + 31) // 32).sum()
-    rec = _mode_record(lay)
+    rec = mode_record(lay)
     assert rec[0] == 0 and rec[2] == blocks
     assert rec[3] == (1 if counts.sum() >= 6 * blocks else 0) == wide
 
@@ -240,14 +239,14 @@ def test_streaming_layouts_short_chunks(T, b, wide):
     import dynamic_expert_sparsity_amd as B
     shape = synth.LayerShape(384, 16, 4, 320, torch.bfloat16)
     L = layer(shape, T, seed=1800 + T, mask_bias=b)
-    y, G, O, _ = _full_check(L, 4, tokens=sample_tokens(T, 64, seed=T))
+    y, G, O, _ = _full_check(L, 4)
     lay = B.MoELayer(L["W_gate"], L["W_mask"], L["W_gu"], L["W_dt"], 4)
     lay(L["x"])
     torch.cuda.synchronize()
     assert lay.sizes["path"] == 0
     counts = G["counts"]
     blocks = ((counts[counts > 0] + 31) // 32).sum()
-    assert _mode_record(lay)[3] == (1 if counts.sum() >= 6 * blocks else 0) == wide
+    assert mode_record(lay)[3] == (1 if counts.sum() >= 6 * blocks else 0) == wide
 
 
 @pytest.mark.parametrize("b", [0.0, 8.0])
@@ -262,7 +261,7 @@ def test_qwen3_prefill_8192(b):
 @pytest.mark.parametrize("T", [1500, 3001])
 def test_router_tiles_large_batch(T):
     L = layer(SMALL, T, seed=1240 + T, mask_bias=0.0)
-    _full_check(L, 2, tokens=sample_tokens(T, 32, seed=6))
+    _full_check(L, 2)
 
 
 # above 8192 tokens the logits come from the router GEMM (128-token tiles):
@@ -270,7 +269,7 @@ def test_router_tiles_large_batch(T):
 @pytest.mark.parametrize("T", [8193, 8300])
 def test_router_gemm_ragged(T):
     L = layer(SMALL, T, seed=1250 + T, mask_bias=0.0)
-    _full_check(L, 2, tokens=sample_tokens(T, 32, seed=5))
+    _full_check(L, 2)
 
 
 # (T = 1024 at keep 0.15: the streaming kernels on the tiled path; T = 4096:
@@ -278,4 +277,4 @@ def test_router_gemm_ragged(T):
 @pytest.mark.parametrize("T,b", [(1, -1.04), (64, 0.0), (1024, -1.04), (4096, -1.04)])
 def test_large_layer(T, b):
     L = layer("large", T, seed=1300 + T, mask_bias=b)
-    _full_check(L, 8, tokens=sample_tokens(T, 24, seed=4))
+    _full_check(L, 8)
