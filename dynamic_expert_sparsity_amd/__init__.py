@@ -18,13 +18,14 @@ __all__ = [
     "BEAM_OK", "BEAM_EINVAL", "BEAM_EUNSUPPORTED", "BEAM_EWORKSPACE", "BEAM_EHIP",
     "BEAM_F32", "BEAM_BF16", "BEAM_FORCE_DECODE", "BEAM_FORCE_PREFILL",
     "STAGES", "BeamError", "lib", "library_path", "Desc", "Routing", "Sizes",
-    "make_desc", "query", "alloc_routing", "route", "forward", "MoELayer", "HipEvents",
-    "RoutingStats",
+    "make_desc", "query", "alloc_routing", "route", "forward", "forward_noalloc", "MoELayer",
+    "HipEvents", "RoutingStats", "NOALLOC_SCRATCH_BYTES",
 ]
 
 BEAM_OK, BEAM_EINVAL, BEAM_EUNSUPPORTED, BEAM_EWORKSPACE, BEAM_EHIP = 0, -1, -2, -3, -4
 BEAM_F32, BEAM_BF16 = 0, 1
 BEAM_FORCE_DECODE, BEAM_FORCE_PREFILL = 1, 2
+NOALLOC_SCRATCH_BYTES = 64 << 20  # beam_moe_forward_noalloc's per-GPU workspace
 STAGES = ["router", "select", "scan", "scatter", "up", "down", "combine"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -89,6 +90,9 @@ def lib() -> ctypes.CDLL:
         L.beam_moe_forward_ex.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, vp, vp, vp,
                                           ctypes.POINTER(Routing), vp, sz, vp, vp]
         L.beam_moe_forward_ex.restype = ctypes.c_int
+        L.beam_moe_forward_noalloc.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, vp, vp, vp,
+                                               ctypes.POINTER(Routing), vp]
+        L.beam_moe_forward_noalloc.restype = ctypes.c_int
         L.beam_moe_mask_backward.argtypes = [ctypes.POINTER(Desc), vp, vp, ctypes.POINTER(Routing),
                                              vp, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp]
         L.beam_moe_mask_backward.restype = ctypes.c_int
@@ -371,3 +375,15 @@ def forward(x, W_gate, W_mask, W_gu, W_dt, K, block_m=0, flags=0, tau=0.0, strea
     R = dict(R)
     R["_ws"] = layer.ws
     return y, R
+
+
+def forward_noalloc(desc: Desc, x, W_gate, W_mask, W_gu, W_dt, y, R: dict, stream=None):
+    """beam_moe_forward_noalloc: the layer into caller-allocated y and routing
+    tensors R (from alloc_routing), with the library's static per-GPU
+    workspace instead of a workspace argument.  Allocates nothing."""
+    for name, t in (("x", x), ("W_gate", W_gate), ("W_mask", W_mask), ("W_gu", W_gu),
+                    ("W_dt", W_dt), ("y", y)):
+        _gpu_tensor(name, t)
+    _check(lib().beam_moe_forward_noalloc(
+        ctypes.byref(desc), x.data_ptr(), W_gate.data_ptr(), W_mask.data_ptr(), W_gu.data_ptr(),
+        W_dt.data_ptr(), y.data_ptr(), ctypes.byref(_routing_struct(R)), _stream_ptr(stream)))

@@ -7,12 +7,20 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "beam_moe.h"
 #include "kernels.h"
 
 using namespace beam;
+
+// Workspace of beam_moe_forward_noalloc: one copy on every GPU the library
+// runs on, allocated when the code object is loaded and held until the
+// process ends.  Host code never uses this name as an address (on the host it
+// is only a stand-in for the symbol): the device address of each GPU's copy
+// comes from hipGetSymbolAddress with that GPU current.
+static __device__ __align__(256) unsigned char scratch[BEAM_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -186,6 +194,32 @@ int check_inputs(const void *x, const void *Wg, const void *Wm) {
     return BEAM_OK;
 }
 
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[MAX_DEVICES] = {};
+
+// The device address of the current GPU's scratch copy, looked up once per
+// device (with that device current) and kept.
+int scratch_address(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(BEAM_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= MAX_DEVICES)
+        return fail(BEAM_EUNSUPPORTED, "device %d is beyond the %d devices the scratch table holds",
+                    dev, MAX_DEVICES);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(BEAM_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return BEAM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -257,6 +291,24 @@ int beam_moe_forward(const beam_moe_desc *desc, const void *x, const void *W_gat
                      const beam_moe_routing *out, void *ws, size_t ws_bytes, hipStream_t stream) {
     return beam_moe_forward_ex(desc, x, W_gate, W_mask, W_gu, W_dt, y, out, ws, ws_bytes, stream,
                                nullptr);
+}
+
+int beam_moe_forward_noalloc(const beam_moe_desc *desc, const void *x, const void *W_gate,
+                             const void *W_mask, const void *W_gu, const void *W_dt, void *y,
+                             const beam_moe_routing *out, hipStream_t stream) {
+    Plan p;
+    int rc = make_plan(desc, p);
+    if (rc) return rc;
+    if (p.total_bytes > (size_t)BEAM_NOALLOC_SCRATCH_BYTES)
+        return fail(BEAM_EWORKSPACE,
+                    "this layer call needs %zu bytes of workspace; the allocation-free entry point "
+                    "holds %zu (use beam_moe_forward with a workspace)",
+                    p.total_bytes, (size_t)BEAM_NOALLOC_SCRATCH_BYTES);
+    if (p.T == 0) return BEAM_OK;
+    void *ws = nullptr;
+    if ((rc = scratch_address(&ws))) return rc;
+    return beam_moe_forward_ex(desc, x, W_gate, W_mask, W_gu, W_dt, y, out, ws,
+                               (size_t)BEAM_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 int beam_moe_mask_backward(const beam_moe_desc *desc, const void *x, const void *W_mask,

@@ -15,7 +15,9 @@
  *   - All tensor pointers are DEVICE pointers owned by the caller, row-major,
  *     16-byte aligned (tensor inputs/outputs) or 4-byte aligned (routing
  *     buffers).  The library never allocates, frees or retains memory, never
- *     synchronises the stream and never reads device memory on the host.
+ *     synchronises the stream and never reads device memory on the host
+ *     (beam_moe_forward_noalloc's static per-GPU workspace aside: it lives
+ *     in the library's code object).
  *   - Work is enqueued on `stream` (0 = the null stream) and runs
  *     asynchronously; a return value of 0 means "enqueued".
  *   - Errors are negative and are detected on the host BEFORE anything is
@@ -23,8 +25,10 @@
  *     call may have been enqueued).  beam_moe_last_error() gives the message
  *     for the calling thread.
  *   - T = 0 is a valid call that enqueues nothing.
- *   - The library holds no mutable global state; calls from several threads
- *     are safe as long as they use distinct output and workspace buffers.
+ *   - The library holds no mutable global state (beyond the static
+ *     workspace of beam_moe_forward_noalloc and its per-GPU address table);
+ *     calls from several threads are safe as long as they use distinct
+ *     output and workspace buffers.
  *
  * Storage layouts (dtype = BEAM_F32: float everywhere; BEAM_BF16: bfloat16):
  *   x       [T, d]
@@ -175,6 +179,27 @@ int beam_moe_forward_ex(const beam_moe_desc *desc, const void *x, const void *W_
                         void *y, const beam_moe_routing *out, void *ws,
                         size_t ws_bytes, hipStream_t stream,
                         hipEvent_t *stage_events);
+
+/* beam_moe_forward_noalloc: beam_moe_forward without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * caller still passes the inputs, y and the routing outputs.  The workspace
+ * is a static array of BEAM_NOALLOC_SCRATCH_BYTES in the library's code
+ * object: one copy per GPU, allocated when the library's code is loaded on
+ * that GPU and held until the process ends.  The call allocates and frees
+ * nothing; its first call on a GPU looks up that GPU's copy (the current
+ * device must be the stream's device).  Every call on one GPU shares that
+ * GPU's copy, which keeps the last call's contents (no part of it needs to
+ * start at zero): calls that may overlap on one GPU (different streams, or
+ * several threads) race and must be serialised by the caller.
+ * Returns BEAM_EWORKSPACE when the call needs more than
+ * BEAM_NOALLOC_SCRATCH_BYTES (sizes.workspace_bytes of beam_moe_query); with
+ * the Qwen3-30B-A3B-shaped layer (d 2048, I 768, E 128, K 8) that holds
+ * batches of up to 512 tokens.  Other errors as for beam_moe_forward. */
+#define BEAM_NOALLOC_SCRATCH_BYTES (64u << 20)
+int beam_moe_forward_noalloc(const beam_moe_desc *desc, const void *x, const void *W_gate,
+                             const void *W_mask, const void *W_gu, const void *W_dt, void *y,
+                             const beam_moe_routing *out, hipStream_t stream);
 
 /* beam_moe_mask_backward: gradients of the mask router for one layer call
  * (BEAM paper, section 3.3: straight-through estimation of the binarisation;

@@ -187,3 +187,25 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError, match="GPU"):
         B.MoELayer(W, W, torch.zeros(16, 128, 256, dtype=torch.bfloat16),
                    torch.zeros(16, 256, 64, dtype=torch.bfloat16), 2)
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch():
+    # host-side checks only: nothing is enqueued, no GPU is touched
+    L = B.lib()
+    big = B.make_desc(8192, 2048, 128, 8, 768, 1)  # tiled path: ~1.4 GB of workspace
+    assert B.query(big)["workspace_bytes"] > B.NOALLOC_SCRATCH_BYTES
+    rc = L.beam_moe_forward_noalloc(ctypes.byref(big), 0x1000, 0x2000, 0x3000, 0x4000, 0x5000,
+                                    0x6000, None, None)
+    assert rc == B.BEAM_EWORKSPACE
+    assert b"allocation-free" in L.beam_moe_last_error()
+    bad = B.make_desc(16, 64, 8, 9, 128, 0)        # K > E
+    rc = L.beam_moe_forward_noalloc(ctypes.byref(bad), 0x1000, 0x2000, 0x3000, 0x4000, 0x5000,
+                                    0x6000, None, None)
+    assert rc == B.BEAM_EINVAL
+
+
+def test_noalloc_scratch_covers_qwen3_decode():
+    # the Qwen3-30B-A3B-shaped layer fits the static workspace up to 512 tokens
+    for T in (1, 64, 256, 512):
+        assert B.query(B.make_desc(T, 2048, 128, 8, 768, 1))["workspace_bytes"] <= \
+            B.NOALLOC_SCRATCH_BYTES
