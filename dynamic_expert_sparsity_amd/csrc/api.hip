@@ -69,15 +69,21 @@ int make_plan(const beam_moe_desc *desc, Plan &p) {
     if (D.dtype == BEAM_BF16 && (D.d % 128 != 0 || D.I % 64 != 0 || D.I > 2040))
         return fail(BEAM_EUNSUPPORTED,
                     "bf16 layer needs d %% 128 == 0, I %% 64 == 0 and I <= 2040 (d=%d I=%d)", D.d, D.I);
-    // the tiled (prefill) path: bf16, 128-position blocks, d % 256, I % 128
-    const bool gemm_ok = D.dtype == BEAM_BF16 && D.d % 256 == 0 && D.I % 128 == 0 &&
-                         (D.block_m == 0 || D.block_m == 128);
-    if ((D.flags & BEAM_FORCE_PREFILL) && !gemm_ok)
-        return fail(BEAM_EUNSUPPORTED,
-                    "the tiled path needs bf16, d %% 256 == 0, I %% 128 == 0, block_m 0 or 128");
     const long long TK = (long long)D.T * D.K;
     const long long PT = (long long)D.T * (D.K + D.n_shared);
     if (PT > (1ll << 30)) return fail(BEAM_EUNSUPPORTED, "T*(K+n_shared)=%lld too large", PT);
+    // the tiled (prefill) path: bf16, 128-position blocks, d % 256, I % 128;
+    // its kernels address x and h with 32-bit byte offsets (below 2^31)
+    const long long max_act_tiled = PT < D.E + D.n_shared ? PT : D.E + D.n_shared;
+    const long long cap_tiled = (PT + max_act_tiled * 127 + 127) / 128 * 128;
+    const bool offsets32 = (long long)D.T * D.d * 2 < (1ll << 31) &&
+                           cap_tiled * D.I * 2 < (1ll << 31);
+    const bool gemm_ok = D.dtype == BEAM_BF16 && D.d % 256 == 0 && D.I % 128 == 0 &&
+                         (D.block_m == 0 || D.block_m == 128) && offsets32;
+    if ((D.flags & BEAM_FORCE_PREFILL) && !gemm_ok)
+        return fail(BEAM_EUNSUPPORTED,
+                    "the tiled path needs bf16, d %% 256 == 0, I %% 128 == 0, block_m 0 or 128, "
+                    "and x and the intermediate rows below 2 GiB");
 
     p.T = D.T; p.d = D.d; p.E = D.E; p.K = D.K; p.I = D.I;
     p.S = D.n_shared; p.E2 = D.E + D.n_shared; p.PT = (int)PT;

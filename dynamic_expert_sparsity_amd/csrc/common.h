@@ -42,6 +42,12 @@ __device__ __forceinline__ float silu(float a) {
     return a / (1.0f + e);
 }
 
+// SiLU with the hardware exp2 and reciprocal (about 1 ulp each), for
+// results rounded to bfloat16.
+__device__ __forceinline__ float silu_fast(float a) {
+    return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a));
+}
+
 // One MFMA: D(16x16 f32) += A(16x32 bf16) * B(32x16 bf16).
 // Lane l supplies A[l % 16][8*(l/16) .. +7] and B[8*(l/16) .. +7][l % 16] and
 // holds D[4*(l/16) + i][l % 16], i = 0..3.

@@ -116,6 +116,10 @@ struct GemmCfg {
     static constexpr int S_PRO = NB == NA + 1 ? LB : L;
     static_assert(NB == NA || (LA - 1) / PER < KK - 1, "A of a stage is sent before its boundary");
     static_assert(S_LOOP < 64 && S_PRO < 64, "vmcnt range");
+    // bf16 stores of one wave's epilogue (UP: SiLU(a) * u of 2 of its 4
+    // column blocks; DOWN: all 4), counted for the next tile's first wait
+    static constexpr int ST_UP = MF * 16 * 2;
+    static constexpr int ST_DOWN = MF * 16 * 4;
 };
 
 enum GemmMode { MODE_UP = 0, MODE_DOWN = 1, MODE_ROUTER = 2 };
@@ -152,6 +156,23 @@ __device__ __forceinline__ void lds_dma16(const void *g, unsigned char *l) {
     __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)l, 16, 0, 0);
 }
 
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// A raw buffer resource over `bytes` bytes from `base` (word 3: the gfx9
+// raw-buffer format); loads at offsets past `bytes` return 0.
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+// 16 bytes per lane from buffer offset voff + soff into LDS (the wave's 1 KB
+// of destinations starts at l).  The buffer form of the LDS DMA is counted
+// in vmcnt only; the flat form is also counted as a possible LDS access,
+// which made the compiler drain every LDS read before the next MFMAs.
+__device__ __forceinline__ void lds_dma16_buf(rsrc_t r, uint32_t voff, uint32_t soff,
+                                              unsigned char *l) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)l, 16,
+                                             voff, soff, 0, 0);
+}
+
 struct GemmArgs {
     const bf16_t *A;        // x (UP, ROUTER) or h (DOWN)
     const bf16_t *W;        // W_gu (UP), W_dt (DOWN), W_gate (ROUTER)
@@ -161,6 +182,7 @@ struct GemmArgs {
     bf16_t *out;            // h (UP) or o (DOWN)
     float *gate_logits, *mask_logits;  // ROUTER
     int T, d, I, E;
+    uint32_t a_bytes;       // bytes of A (UP: x, DOWN: h; below 2^31)
     int n_ntiles;           // column tiles per block
     int n_rblocks;          // ROUTER: row blocks
     const int32_t *mode;    // UP/DOWN: the call's record {family, max count, records, 0}
@@ -214,207 +236,238 @@ __global__ __launch_bounds__(BM / WT * 128, 1) void grouped_gemm(GemmArgs g) {
         for (int n = 0; n < 4; ++n) brow[n] = wn * 128 + n * 32;
     }
 
-    for (int tile = t_begin + (int)(blockIdx.x >> 3); tile < t_end; tile += per_xcd_wg) {
+    // One tile's place in the problem and its operand addresses.  UP/DOWN
+    // address their operands through buffer resources (32-bit byte offsets
+    // per lane; the stage's k offset goes in the scalar offset), the router
+    // through pointers.
+    struct Tile {
+        int pos0, nt, seg, rows_valid;
+        bool live;
+        unsigned a_send;   // bit u: A load u has a valid row (wave-uniform)
+        rsrc_t rB;         // UP/DOWN: the expert's weights
+        uint32_t offA[C::LA], offB[C::LB];
+        const bf16_t *srcA[MODE == MODE_ROUTER ? C::LA : 1], *srcB[MODE == MODE_ROUTER ? C::LB : 1];
+    };
+    const rsrc_t rA = make_rsrc(g.A, g.a_bytes);
+    // A loads whose 8 rows all lie past the tile's valid rows are not
+    // sent (SKIP_A): no MFMA result that is stored for a real pair reads
+    // them (a row's products depend on that row only; pad rows of a
+    // segment are written but never read), and with NB = NA + 1 every
+    // wait allows only B loads to be outstanding, which are always sent
+    // (so a missing A load never shortens a wait).  Keeps the weight
+    // stream and drops the DMA of a part-filled tile's empty rows.
+    constexpr bool SKIP_A = G_SKIP_A && MODE != MODE_ROUTER && NB == NA + 1;
+
+    auto setup = [&](int tile, Tile &t) {
         const int blk = tile / g.n_ntiles;
-        const int nt = tile - blk * g.n_ntiles;
+        t.nt = tile - blk * g.n_ntiles;
         // tile: BM rows from pos0 of expert e; seg of them lie in the expert's
         // padded segment (a 256-row tile can end after 128), rows_valid hold
         // real pairs (tokens, for the router)
-        int pos0, e, seg, rows_valid;
+        int e;
         if (MODE == MODE_ROUTER) {
-            pos0 = blk * BM;
+            t.pos0 = blk * BM;
             e = 0;
-            seg = BM;
-            rows_valid = g.T - pos0;
+            t.seg = BM;
+            t.rows_valid = g.T - t.pos0;
         } else if (BM == 256) {
             const int4 rec = *reinterpret_cast<const int4 *>(g.pbt + 4 * blk);
             e = rec.x;
-            pos0 = rec.y;
-            seg = rec.z;
-            rows_valid = rec.w;
+            t.pos0 = rec.y;
+            t.seg = rec.z;
+            t.rows_valid = rec.w;
         } else {
-            pos0 = blk * BM;
+            t.pos0 = blk * BM;
             e = g.block_expert[blk];
-            seg = BM;
-            rows_valid = g.expert_offsets[e] + g.expert_counts[e] - pos0;
+            t.seg = BM;
+            t.rows_valid = g.expert_offsets[e] + g.expert_counts[e] - t.pos0;
         }
-        const bool live = __builtin_amdgcn_readfirstlane(wm * WT < rows_valid ? 1 : 0) != 0;
-
+        t.live = __builtin_amdgcn_readfirstlane(wm * WT < t.rows_valid ? 1 : 0) != 0;
+        if (MODE != MODE_ROUTER) {
+            const size_t wrows = MODE == MODE_UP ? (size_t)2 * g.I : (size_t)g.d;
+            t.rB = make_rsrc(g.W + (size_t)e * wrows * ldw, (uint32_t)(wrows * ldw * 2));
+        }
         // this lane's 16 bytes land at slot l % 8 of row r: chunk (l % 8) ^ f(r)
-        const bf16_t *srcA[C::LA], *srcB[C::LB];
 #pragma unroll
         for (int i = 0; i < C::LA; ++i) {
             const int r = G_RPI * (wave + C::NW * i) + lrow;
             // rows past the segment (the next expert's, or past the lists)
             // read the segment's first row; nothing stores them
-            const int rs = r < seg ? r : 0;
+            const int rs = r < t.seg ? r : 0;
+            const int ch = ((lane & 7) ^ swz_f(r)) * 8;
             if (MODE == MODE_UP) {
-                srcA[i] = g.A + (size_t)g.sorted_tok[pos0 + rs] * g.d;
+                t.offA[i] = ((uint32_t)g.sorted_tok[t.pos0 + rs] * (uint32_t)g.d + ch) * 2u;
             } else if (MODE == MODE_DOWN) {
-                srcA[i] = g.A + (size_t)(pos0 + rs) * g.I;
+                t.offA[i] = ((uint32_t)(t.pos0 + rs) * (uint32_t)g.I + ch) * 2u;
             } else {
-                const int t = min(pos0 + r, g.T - 1);
-                srcA[i] = g.A + (size_t)t * g.d;
+                const int tk = min(t.pos0 + r, g.T - 1);
+                t.srcA[i] = g.A + (size_t)tk * g.d + ch;
             }
-            srcA[i] += ((lane & 7) ^ swz_f(r)) * 8;
         }
 #pragma unroll
         for (int i = 0; i < C::LB; ++i) {
             const int r = G_RPI * (wave + C::NW * i) + lrow;
+            const int ch = ((lane & 7) ^ swz_f(r)) * 8;
             if (MODE == MODE_UP) {
-                const int wr = r < 128 ? nt * 128 + r : g.I + nt * 128 + (r - 128);
-                srcB[i] = g.W + ((size_t)e * 2 * g.I + wr) * ldw;
+                const int wr = r < 128 ? t.nt * 128 + r : g.I + t.nt * 128 + (r - 128);
+                t.offB[i] = ((uint32_t)wr * (uint32_t)ldw + ch) * 2u;
             } else if (MODE == MODE_DOWN) {
-                srcB[i] = g.W + ((size_t)e * g.d + nt * GBN + r) * ldw;
+                t.offB[i] = ((uint32_t)(t.nt * GBN + r) * (uint32_t)ldw + ch) * 2u;
             } else {
-                const int n = min(nt * GBN + r, 2 * g.E - 1);
-                srcB[i] = n < g.E ? g.W + (size_t)n * ldw : g.W2 + (size_t)(n - g.E) * ldw;
+                const int n = min(t.nt * GBN + r, 2 * g.E - 1);
+                t.srcB[i] = (n < g.E ? g.W + (size_t)n * ldw : g.W2 + (size_t)(n - g.E) * ldw) + ch;
             }
-            srcB[i] += ((lane & 7) ^ swz_f(r)) * 8;
         }
-        // issue slot p (stage p of the loop; p < 0 before it) loads A of stage
-        // p + NA - 1 and then B of stage p + NB - 1, each into the ring buffer
-        // the stage before it left free at the last boundary
-        // A loads whose 8 rows all lie past the tile's valid rows are not
-        // sent (SKIP_A): no MFMA result that is stored for a real pair reads
-        // them (a row's products depend on that row only; pad rows of a
-        // segment are written but never read), and with NB = NA + 1 every
-        // wait allows only B loads to be outstanding, which are always sent
-        // (so a missing A load never shortens a wait).  Keeps the weight
-        // stream and drops the DMA of a part-filled tile's empty rows.
-        constexpr bool SKIP_A = G_SKIP_A && MODE != MODE_ROUTER && NB == NA + 1;
-        unsigned a_send = 0;  // bit u: A load u has a valid row (wave-uniform)
+        t.a_send = 0;
 #pragma unroll
         for (int i = 0; i < C::LA; ++i)
-            if (!SKIP_A || G_RPI * (wave + C::NW * i) < rows_valid) a_send |= 1u << i;
-        auto issue = [&](int p, int u) {
-            if (u < C::LA) {
-                const int j = p + NA - 1;
-                if (j >= 0 && j < nst && ((a_send >> u) & 1u))
-                    lds_dma16(srcA[u] + j * GBK,
-                              lds + (j % NA) * C::A_BYTES + (wave + C::NW * u) * 1024);
-            } else {
-                const int j = p + NB - 1;
-                if (j >= 0 && j < nst)
-                    lds_dma16(srcB[u - C::LA] + j * GBK,
-                              lds + C::B_OFF + (j % NB) * C::B_BYTES + (wave + C::NW * (u - C::LA)) * 1024);
-            }
-        };
+            if (!SKIP_A || G_RPI * (wave + C::NW * i) < t.rows_valid) t.a_send |= 1u << i;
+    };
 
-        f32x16 acc[MF][4];
+    // issue slot p (stage p of the loop; p < 0 before it) loads A of stage
+    // p + NA - 1 and then B of stage p + NB - 1, each into the ring buffer
+    // the stage before it left free at the last boundary
+    auto issue = [&](const Tile &t, int p, int u) {
+        if (u < C::LA) {
+            const int j = p + NA - 1;
+            if (j >= 0 && j < nst && ((t.a_send >> u) & 1u)) {
+                unsigned char *dst = lds + (j % NA) * C::A_BYTES + (wave + C::NW * u) * 1024;
+                if constexpr (MODE == MODE_ROUTER) lds_dma16(t.srcA[u] + j * GBK, dst);
+                else lds_dma16_buf(rA, t.offA[u], (uint32_t)j * G_ROWB, dst);
+            }
+        } else {
+            const int j = p + NB - 1;
+            if (j >= 0 && j < nst) {
+                unsigned char *dst =
+                    lds + C::B_OFF + (j % NB) * C::B_BYTES + (wave + C::NW * (u - C::LA)) * 1024;
+                if constexpr (MODE == MODE_ROUTER) lds_dma16(t.srcB[u - C::LA] + j * GBK, dst);
+                else lds_dma16_buf(t.rB, t.offB[u - C::LA], (uint32_t)j * G_ROWB, dst);
+            }
+        }
+    };
+    auto prologue = [&](const Tile &t) {
+        for (int p = -(NB - 1); p < 0; ++p)
+#pragma unroll
+            for (int u = 0; u < C::L; ++u) issue(t, p, u);
+    };
+
+    f32x16 acc[MF][4];
+    // fragments of one 16-wide k-slice, in two alternating sets
+    u32x4 af[2][MF], bfr[2][4];
+    auto read_frags = [&](int s, int kk, int set) {
+        const unsigned char *sa = lds + (s % NA) * C::A_BYTES;
+        const unsigned char *sb = lds + C::B_OFF + (s % NB) * C::B_BYTES;
+        const int ch = 2 * kk + lh;
 #pragma unroll
         for (int m = 0; m < MF; ++m)
+            af[set][m] = *reinterpret_cast<const u32x4 *>(sa + swz(wm * WT + m * 32 + lr, ch));
 #pragma unroll
-            for (int n = 0; n < 4; ++n)
+        for (int n = 0; n < 4; ++n)
+            bfr[set][n] = *reinterpret_cast<const u32x4 *>(sb + swz(brow[n] + lr, ch));
+    };
+    // one k-slice of stage s: the MF x 4 MFMAs (LIVE waves) with the
+    // loads of issue slot s interleaved (spread over the first DKK
+    // slices, one after every few MFMAs, so the address unit works while
+    // the matrix cores do)
+    constexpr int PER = C::PER;
+    constexpr int MPS = C::MPS;
+    auto slice = [&](const Tile &t, auto LIVE, int set, int s, int kk) {
 #pragma unroll
-                for (int v = 0; v < 16; ++v) acc[m][n][v] = 0.f;
-
-        // fragments of one 16-wide k-slice, in two alternating sets
-        u32x4 af[2][MF], bfr[2][4];
-        auto read_frags = [&](int s, int kk, int set) {
-            const unsigned char *sa = lds + (s % NA) * C::A_BYTES;
-            const unsigned char *sb = lds + C::B_OFF + (s % NB) * C::B_BYTES;
-            const int ch = 2 * kk + lh;
-#pragma unroll
-            for (int m = 0; m < MF; ++m)
-                af[set][m] = *reinterpret_cast<const u32x4 *>(sa + swz(wm * WT + m * 32 + lr, ch));
-#pragma unroll
-            for (int n = 0; n < 4; ++n)
-                bfr[set][n] = *reinterpret_cast<const u32x4 *>(sb + swz(brow[n] + lr, ch));
-        };
-        // one k-slice of stage s: the MF x 4 MFMAs (LIVE waves) with the
-        // loads of issue slot s interleaved (spread over the first DKK
-        // slices, one after every few MFMAs, so the address unit works while
-        // the matrix cores do)
-        constexpr int PER = C::PER;
-        constexpr int MPS = C::MPS;
-        auto slice = [&](auto LIVE, int set, int s, int kk) {
-#pragma unroll
-            for (int j = 0; j < MPS; ++j) {
-                const int m = j >> 2, n = j & 3;
-                if constexpr (decltype(LIVE)::value)
-                    acc[m][n] = mfma32x32x16(af[set][m], bfr[set][n], acc[m][n]);
-                if (kk < DKK && (j % (MPS / PER)) == 0) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    issue(s, kk * PER + j / (MPS / PER));
-                    __builtin_amdgcn_sched_barrier(0);
-                }
+        for (int j = 0; j < MPS; ++j) {
+            const int m = j >> 2, n = j & 3;
+            if constexpr (decltype(LIVE)::value)
+                acc[m][n] = mfma32x32x16(af[set][m], bfr[set][n], acc[m][n]);
+            if (kk < DKK && (j % (MPS / PER)) == 0) {
+                __builtin_amdgcn_sched_barrier(0);
+                issue(t, s, kk * PER + j / (MPS / PER));
+                __builtin_amdgcn_sched_barrier(0);
             }
-        };
+        }
+    };
 
-        // Waves whose rows are all padding run the same loop without reads
-        // and MFMAs (a separate copy, so the live copy is straight-line code).
-        auto main_loop = [&](auto LIVE) {
-            constexpr bool LV = decltype(LIVE)::value;
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_s_barrier();  // every wave is done with the previous tile's LDS
-            asm volatile("" ::: "memory");
-            for (int p = -(NB - 1); p < 0; ++p)
+    // The stages of one tile whose prologue loads were issued.  Waves whose
+    // rows are all padding run the same loop without reads and MFMAs (a
+    // separate copy, so the live copy is straight-line code).  The waits
+    // count this wave's vector-memory operations, which complete in issue
+    // order: the epilogue stores of the previous tile, issued after this
+    // tile's prologue loads, are the newest (up to ST of them).
+    auto main_loop = [&](const Tile &t, auto LIVE, int stores_after_prologue) {
+        constexpr bool LV = decltype(LIVE)::value;
+        if (stores_after_prologue) {
+            // every prologue load is older than the stores: all of them done
+            // once at most min(stores, 63) operations are in flight, which
+            // also lets the newest stage's B loads finish (a stricter wait)
+            if constexpr (MODE == MODE_ROUTER) wait_vmcnt<0>();
+            else wait_vmcnt<(MODE == MODE_UP ? C::ST_UP : C::ST_DOWN) < 63
+                                 ? (MODE == MODE_UP ? C::ST_UP : C::ST_DOWN) : 63>();
+        } else if (1 < nst) {
+            wait_vmcnt<C::S_PRO>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if constexpr (LV) read_frags(0, 0, 0);
+        for (int s = 0; s < nst; ++s) {
 #pragma unroll
-                for (int u = 0; u < C::L; ++u) issue(p, u);
-            if (1 < nst) wait_vmcnt<C::S_PRO>();
-            else wait_vmcnt<0>();
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_s_barrier();
-            asm volatile("" ::: "memory");
-            if constexpr (LV) read_frags(0, 0, 0);
-            for (int s = 0; s < nst; ++s) {
-#pragma unroll
-                for (int kk = 0; kk < KK; ++kk) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    if (kk + 1 < KK) {
-                        if constexpr (LV) read_frags(s, kk + 1, (kk + 1) & 1);
-                    } else if (s + 1 < nst) {
-                        // stage boundary: stage s + 1 landed for every wave,
-                        // stage s read by every wave
-                        if (s + 2 < nst) wait_vmcnt<C::S_LOOP>();
-                        else wait_vmcnt<0>();
-                        if constexpr (LV) wait_lgkm<0>();
-                        asm volatile("" ::: "memory");
-                        __builtin_amdgcn_s_barrier();
-                        asm volatile("" ::: "memory");
-                        if constexpr (LV) read_frags(s + 1, 0, 0);
-                    }
-                    // the slice's own fragments are in (LDS reads complete in
-                    // order; only the MF + 4 reads of the next slice may be
-                    // pending)
-                    if constexpr (LV) wait_lgkm<MF + 4>();
-                    __builtin_amdgcn_sched_barrier(0);
-                    slice(LIVE, kk & 1, s, kk);
+            for (int kk = 0; kk < KK; ++kk) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (kk + 1 < KK) {
+                    if constexpr (LV) read_frags(s, kk + 1, (kk + 1) & 1);
+                } else if (s + 1 < nst) {
+                    // stage boundary: stage s + 1 landed for every wave,
+                    // stage s read by every wave
+                    if (s + 2 < nst) wait_vmcnt<C::S_LOOP>();
+                    else wait_vmcnt<0>();
+                    if constexpr (LV) wait_lgkm<0>();
+                    asm volatile("" ::: "memory");
+                    __builtin_amdgcn_s_barrier();
+                    asm volatile("" ::: "memory");
+                    if constexpr (LV) read_frags(s + 1, 0, 0);
                 }
+                // the slice's own fragments are in (LDS reads complete in
+                // order; only the MF + 4 reads of the next slice may be
+                // pending)
+                if constexpr (LV) wait_lgkm<MF + 4>();
+                __builtin_amdgcn_sched_barrier(0);
+                slice(t, LIVE, kk & 1, s, kk);
             }
-        };
-        if (live) main_loop(std::true_type{});
-        else main_loop(std::false_type{});
+        }
+    };
 
-        // epilogue: D[i][j] of a 32x32 tile sits in lane j + 32*((i/4) % 2),
-        // register 4*(i/8) + i%4.  Pad rows of a block compute values nothing
-        // reads (their A rows are token 0 / h rows inside the buffer).
+    // epilogue: D[i][j] of a 32x32 tile sits in lane j + 32*((i/4) % 2),
+    // register 4*(i/8) + i%4.  Pad rows of a block compute values nothing
+    // reads (their A rows are token 0 / h rows inside the buffer).  A wave's
+    // rows lie wholly inside or wholly past the segment (segments are
+    // multiples of 128 rows, wave rows WT <= 64 aligned), so each wave
+    // issues all of its C::ST stores or none.
+    auto epilogue = [&](const Tile &t) {
+        if (MODE != MODE_ROUTER && wm * WT >= t.seg) return;  // the next expert's rows
 #pragma unroll
         for (int m = 0; m < MF; ++m) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int row = wm * WT + m * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-                const size_t prow = (size_t)(pos0 + row);
-                if (MODE != MODE_ROUTER && row >= seg) continue;  // the next expert's rows
+                const size_t prow = (size_t)(t.pos0 + row);
                 if (MODE == MODE_UP) {
 #pragma unroll
                     for (int n = 0; n < 2; ++n) {
-                        const int j = nt * 128 + wn * 64 + n * 32 + lr;
+                        const int j = t.nt * 128 + wn * 64 + n * 32 + lr;
                         g.out[prow * g.I + j] =
-                            f32_to_bf16(silu<false>(acc[m][n][v]) * acc[m][n + 2][v]);
+                            f32_to_bf16(silu_fast(acc[m][n][v]) * acc[m][n + 2][v]);
                     }
                 } else if (MODE == MODE_DOWN) {
 #pragma unroll
                     for (int n = 0; n < 4; ++n) {
-                        const int c = nt * GBN + wn * 128 + n * 32 + lr;
+                        const int c = t.nt * GBN + wn * 128 + n * 32 + lr;
                         g.out[prow * g.d + c] = f32_to_bf16(acc[m][n][v]);
                     }
                 } else {
                     if ((int)prow < g.T) {
 #pragma unroll
                         for (int n = 0; n < 4; ++n) {
-                            const int c = nt * GBN + wn * 128 + n * 32 + lr;
+                            const int c = t.nt * GBN + wn * 128 + n * 32 + lr;
                             if (c < g.E) g.gate_logits[prow * g.E + c] = acc[m][n][v];
                             else if (c < 2 * g.E) g.mask_logits[prow * g.E + (c - g.E)] = acc[m][n][v];
                         }
@@ -422,6 +475,42 @@ __global__ __launch_bounds__(BM / WT * 128, 1) void grouped_gemm(GemmArgs g) {
                 }
             }
         }
+    };
+
+    int tile = t_begin + (int)(blockIdx.x >> 3);
+    if (tile >= t_end) return;
+    Tile cur;
+    setup(tile, cur);
+    prologue(cur);
+    int stores = 0;  // epilogue stores issued after the current tile's prologue
+    for (;;) {
+#pragma unroll
+        for (int m = 0; m < MF; ++m)
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[m][n][v] = 0.f;
+        if (cur.live) main_loop(cur, std::true_type{}, stores);
+        else main_loop(cur, std::false_type{}, stores);
+        // the next tile's loads go out before this tile's epilogue, so they
+        // overlap its arithmetic and stores; first every wave is done
+        // reading this tile's stages
+        const int next = tile + per_xcd_wg;
+        const bool more = next < t_end;
+        Tile nxt;
+        if (more) {
+            setup(next, nxt);
+            wait_lgkm<0>();
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            prologue(nxt);
+        }
+        epilogue(cur);
+        if (!more) break;
+        stores = MODE != MODE_ROUTER && wm * WT >= cur.seg ? 0 : 1;
+        cur = nxt;
+        tile = next;
     }
 }
 
@@ -472,6 +561,7 @@ hipError_t launch_gemm_up(const Plan &p, const void *x, const void *W_gu, const 
                           const Work &w, hipStream_t s) {
     GemmArgs a = base_args(p, r, w);
     a.A = (const bf16_t *)x;
+    a.a_bytes = (uint32_t)((size_t)p.T * p.d * 2);
     a.W = (const bf16_t *)W_gu;
     a.out = (bf16_t *)w.h;
     a.n_ntiles = p.I / (GBN / 2);
@@ -485,6 +575,7 @@ hipError_t launch_gemm_down(const Plan &p, const void *W_dt, const Routing &r, c
                             hipStream_t s) {
     GemmArgs a = base_args(p, r, w);
     a.A = (const bf16_t *)w.h;
+    a.a_bytes = (uint32_t)((size_t)p.cap * p.I * 2);
     a.W = (const bf16_t *)W_dt;
     a.out = (bf16_t *)w.o;
     a.n_ntiles = p.d / GBN;
@@ -497,6 +588,7 @@ hipError_t launch_gemm_router(const Plan &p, const void *x, const void *Wg, cons
                               const Routing &r, hipStream_t s) {
     GemmArgs a{};
     a.A = (const bf16_t *)x;
+    a.a_bytes = 0;  // the router's operands go through pointers
     a.W = (const bf16_t *)Wg;
     a.W2 = (const bf16_t *)Wm;
     a.gate_logits = r.gate_logits;
