@@ -167,10 +167,11 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
 // of destinations starts at l).  The buffer form of the LDS DMA is counted
 // in vmcnt only; the flat form is also counted as a possible LDS access,
 // which made the compiler drain every LDS read before the next MFMAs.
+template <int AUX = 0>
 __device__ __forceinline__ void lds_dma16_buf(rsrc_t r, uint32_t voff, uint32_t soff,
                                               unsigned char *l) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)l, 16,
-                                             voff, soff, 0, 0);
+                                             voff, soff, 0, AUX);
 }
 
 struct GemmArgs {
@@ -340,8 +341,12 @@ __global__ __launch_bounds__(BM / WT * 128, 1) void grouped_gemm(GemmArgs g) {
             if (j >= 0 && j < nst) {
                 unsigned char *dst =
                     lds + C::B_OFF + (j % NB) * C::B_BYTES + (wave + C::NW * (u - C::LA)) * 1024;
+                // 128-row tiles are taken when most experts fill one block:
+                // a weight slice is then read by one tile only and streams
+                // past the L2 (non-temporal); the 256-row tiles of an expert
+                // with several of them share its slices through the L2
                 if constexpr (MODE == MODE_ROUTER) lds_dma16(t.srcB[u - C::LA] + j * GBK, dst);
-                else lds_dma16_buf(t.rB, t.offB[u - C::LA], (uint32_t)j * G_ROWB, dst);
+                else lds_dma16_buf<BM == 128 ? 2 : 0>(t.rB, t.offB[u - C::LA], (uint32_t)j * G_ROWB, dst);
             }
         }
     };
