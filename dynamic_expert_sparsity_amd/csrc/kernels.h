@@ -63,11 +63,12 @@ hipError_t launch_route(const Plan &p, const void *x, const void *Wg, const void
                         const Routing &r, const Work &w, hipStream_t s);
 // pair scatter for large batches (no-op when the routing kernel placed them)
 hipError_t launch_scatter(const Plan &p, const Routing &r, const Work &w, hipStream_t s);
-// prefill path: grouped MFMA GEMMs over 256-position blocks
-hipError_t launch_gemm_up(const Plan &p, const void *x, const void *W_gu, const Routing &r,
-                          const Work &w, hipStream_t s);
-hipError_t launch_gemm_down(const Plan &p, const void *W_dt, const Routing &r, const Work &w,
-                            hipStream_t s);
+// the tiled path (bf16): one launch per projection runs the kernel family
+// the compaction picked for the call (streaming, 128-row or 256-row tiles)
+hipError_t launch_tiled_up(const Plan &p, const void *x, const void *W_gu, const Routing &r,
+                           const Work &w, hipStream_t s);
+hipError_t launch_tiled_down(const Plan &p, const void *W_dt, const Routing &r, const Work &w,
+                             hipStream_t s);
 hipError_t launch_gemm_router(const Plan &p, const void *x, const void *Wg, const void *Wm,
                               const Routing &r, hipStream_t s);
 hipError_t launch_expert_up(const Plan &p, const void *x, const void *W_gu, const Routing &r,
