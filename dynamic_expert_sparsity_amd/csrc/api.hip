@@ -38,6 +38,25 @@ int fail(int code, const char *fmt, ...) {
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+}  // namespace
+
+namespace beam {
+int device_cus() {
+    static int n = 0;
+    static std::once_flag once;
+    std::call_once(once, [] {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+            n = cus;
+        if (n <= 0) n = 256;
+    });
+    return n;
+}
+}  // namespace beam
+
+namespace {
+
 bool aligned(const void *p, size_t a) { return p && (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Validate a descriptor and build the plan (host only).
@@ -102,6 +121,11 @@ int make_plan(const beam_moe_desc *desc, Plan &p) {
     // m = [sigmoid(z) >= tau]  <=>  z >= ln(tau / (1 - tau)); exactly 0 at tau = 0.5
     p.thr = tau == 0.5f ? 0.f : (float)std::log((double)tau / (1.0 - (double)tau));
 
+    // small decode batches: routing + up projection in one launch, down
+    // projection + combine in one (x and the token's h rows fit LDS)
+    p.small = D.dtype == BEAM_BF16 && p.path == 0 && D.T <= SMALL_DECODE_T &&
+              D.K + D.n_shared <= SMALL_SLOTS && (long long)D.T * D.d * 2 <= 48 * 1024 &&
+              (long long)(D.K + D.n_shared) * D.I * 2 <= 48 * 1024;
     p.s_ts = 64;
     p.n_tiles = (D.T + 63) / 64;
     p.fuse_scatter = p.n_tiles <= 16;
@@ -281,6 +305,18 @@ int beam_moe_forward_ex(const beam_moe_desc *desc, const void *x, const void *W_
 
     const Work w = carve(p, ws);
     const Events ev{stage_events, stream};
+    if (p.small) {
+        // logits; then routing + up projection; then down projection + combine
+        BEAM_TRY(ev.mark(BEAM_STAGE_ROUTER), "event");
+        BEAM_TRY(launch_router_logits(p, x, W_gate, W_mask, r, stream), "router logits");
+        for (int st = BEAM_STAGE_SELECT; st <= BEAM_STAGE_UP; ++st) BEAM_TRY(ev.mark(st), "event");
+        BEAM_TRY(launch_up_small(p, x, W_gu, r, w, stream), "routing and expert up");
+        BEAM_TRY(ev.mark(BEAM_STAGE_DOWN), "event");
+        BEAM_TRY(launch_down_small(p, W_dt, r, w, y, stream), "expert down and combine");
+        BEAM_TRY(ev.mark(BEAM_STAGE_COMBINE), "event");
+        BEAM_TRY(ev.mark(BEAM_NUM_STAGES), "event");
+        return BEAM_OK;
+    }
     if ((rc = enqueue_route(p, x, W_gate, W_mask, r, w, stream, ev))) return rc;
     BEAM_TRY(ev.mark(BEAM_STAGE_UP), "event");
     BEAM_TRY(launch_expert_up(p, x, W_gu, r, w, stream), "expert up");

@@ -48,6 +48,35 @@ __device__ __forceinline__ float silu_fast(float a) {
     return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a));
 }
 
+// Sum over the 64 lanes of a wave, in a fixed order (deterministic): within
+// each row of 16 lanes by DPP moves (swap neighbours, swap pairs, mirror
+// within 8, mirror within 16; both partners of a step add the same pair),
+// then the four row sums in row order.  Every lane gets the result.
+__device__ __forceinline__ float wave_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
+           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16)) +
+           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)) +
+           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+}
+
+// Dot product of 8 bf16 pairs (16-byte chunks) added to acc, float32.  Each
+// 32-bit element is copied to a scalar before the bit cast: a bit cast taken
+// directly of a vector element compiled to the first element every time.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot8_bf16(const u32x4 &a, const u32x4 &b, float acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t ai = a[i], bi = b[i];
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, ai),
+                                              __builtin_bit_cast(bf16x2_t, bi), acc, false);
+    }
+    return acc;
+}
+
 // One MFMA: D(16x16 f32) += A(16x32 bf16) * B(32x16 bf16).
 // Lane l supplies A[l % 16][8*(l/16) .. +7] and B[8*(l/16) .. +7][l % 16] and
 // holds D[4*(l/16) + i][l % 16], i = 0..3.

@@ -54,9 +54,13 @@ __device__ __forceinline__ int wave_incl_scan(int v, int /*lane*/) {
 // one record {expert, first position, segment rows, valid rows} per 256-row
 // tile of an expert's 128-padded segment (the last may hold 128 rows); the
 // 128-row tiled kernels (family 1) walk the block map.
+// write = false: only s_off (and, when given, the active-expert list s_act
+// and its length *s_nact) in LDS; nothing in global memory.
 __device__ __forceinline__ void offsets_from_counts(const int *s_cnt, int *s_off, int E, int bm,
                                                     const Routing &r, int32_t *meta,
-                                                    int32_t *pbt, int split, int lane) {
+                                                    int32_t *pbt, int split, int lane,
+                                                    bool write = true, int *s_act = nullptr,
+                                                    int *s_nact = nullptr) {
     int c[4], pad[4], act[4], npb[4], nq[4];
     int sc = 0, sp = 0, sa = 0, mx = 0, sb = 0, sq = 0;
 #pragma unroll
@@ -111,6 +115,9 @@ __device__ __forceinline__ void offsets_from_counts(const int *s_cnt, int *s_off
         const int ex = lane * 4 + j;
         if (ex < E) {
             s_off[ex] = op;
+            if (s_act && act[j]) s_act[oa] = ex;
+        }
+        if (ex < E && write) {
             r.expert_offsets[ex] = op;
             r.expert_counts[ex] = c[j];
             if (act[j]) r.active_experts[oa] = ex;
@@ -131,6 +138,9 @@ __device__ __forceinline__ void offsets_from_counts(const int *s_cnt, int *s_off
     }
     if (lane == 63) {
         s_off[E] = ip;
+        if (s_nact) *s_nact = ia;
+    }
+    if (lane == 63 && write) {
         r.expert_offsets[E] = ip;
         r.num_active[0] = ic;
         r.num_active[1] = ip;

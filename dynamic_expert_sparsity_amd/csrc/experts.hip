@@ -197,6 +197,130 @@ static hipError_t launch_ring(const void *A, const void *W, const Plan &p, const
                            : launch_ring_t<DOWN, true>(A, W, p, w, out, klen, ncols, s);
 }
 
+// ---------------------------------------------------------------------------
+// Down projection and combine of a decode batch of at most SMALL_DECODE_T
+// tokens (Eq. 3 and Eq. 8), token-major: workgroup b owns token t = b / NG
+// and a range of C output channels.  The token's slots (its S shared experts
+// with weight 1, then its active routed slots k in order with weight g_hat)
+// and their h rows are staged in LDS.  The items (slot q, channel c) are
+// spread over the waves, eight at a time per wave with every row piece
+// requested before any arithmetic: each streams row c of the slot's W_dt
+// (16-byte loads), dots it with the slot's h row and sums the lanes in a
+// fixed order into o[q][c] in LDS.  Then each channel adds its slots in slot
+// order (float32, no atomics) and writes y[t][c].  With a few tokens the
+// experts' rows are read once per token that uses them, about once per
+// active expert.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(512) void down_small(int T, int K, int S, int E, int d, int I, int NG,
+                                                  const int32_t *__restrict__ masked_ids,
+                                                  const float *__restrict__ g_hat,
+                                                  const int32_t *__restrict__ pair_pos,
+                                                  const bf16_t *__restrict__ h,
+                                                  const bf16_t *__restrict__ Wdt,
+                                                  bf16_t *__restrict__ y) {
+    __shared__ int s_e[SMALL_SLOTS], s_pos[SMALL_SLOTS];
+    __shared__ float s_w[SMALL_SLOTS];
+    __shared__ int s_n;
+    // [slots][I] bf16 h rows, then [slots][per] float slot outputs
+    extern __shared__ __align__(16) unsigned char dyn[];
+    u32x4 *hs = reinterpret_cast<u32x4 *>(dyn);
+    const int t = blockIdx.x / NG, grp = blockIdx.x - t * NG;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int per = (d + NG - 1) / NG;
+    float *so = reinterpret_cast<float *>(dyn + (size_t)(K + S) * I * 2);
+    if (tid < 64) {
+        // lane l < S: shared expert l (weight 1); S <= l < S + K: routed slot
+        // l - S (its expert id, or -1 if masked); every lane loads its own
+        // slot at once, and the active ones are packed in slot order
+        int e = -1, pos = 0;
+        float wgt = 1.f;
+        if (lane < S) {
+            e = E + lane;
+            pos = pair_pos[T * K + t * S + lane];
+        } else if (lane < S + K) {
+            const int k = lane - S;
+            e = masked_ids[t * K + k];
+            if (e >= 0) {
+                pos = pair_pos[t * K + k];
+                wgt = g_hat[t * K + k];
+            }
+        }
+        const unsigned long long act = __ballot(e >= 0);
+        if (e >= 0) {
+            const int idx = __popcll(act & ((1ull << lane) - 1ull));
+            s_e[idx] = e;
+            s_pos[idx] = pos;
+            s_w[idx] = wgt;
+        }
+        if (lane == 0) s_n = __popcll(act);
+    }
+    __syncthreads();
+    const int n = s_n;
+    const int nch = I >> 3;  // 16-byte chunks per row
+    for (int i = tid; i < n * nch; i += 512) {
+        const int q = i / nch, ch = i - q * nch;
+        hs[i] = ld16(h + (size_t)s_pos[q] * I + (size_t)ch * 8);
+    }
+    __syncthreads();
+    const int c_begin = grp * per, c_end = min(d, c_begin + per);
+    const int C = c_end > c_begin ? c_end - c_begin : 0;
+    const int n_items = n * C;
+    constexpr int IU = 8;  // items per wave at a time
+    // every load is issued (past the end: item i0 / the row's first chunk
+    // again, in bounds and unused), so the compiler keeps all of them in
+    // flight
+    const int ch0 = lane < nch ? lane : 0;
+    const int ch1 = lane + 64 < nch ? lane + 64 : 0;
+    for (int i0 = wave * IU; i0 < n_items; i0 += 8 * IU) {
+        u32x4 wv[IU][2];
+        int qv[IU], cv[IU];
+#pragma unroll
+        for (int u = 0; u < IU; ++u) {
+            const int it = i0 + u < n_items ? i0 + u : i0;
+            qv[u] = it / C;
+            cv[u] = c_begin + (it - qv[u] * C);
+            const bf16_t *wr = Wdt + ((size_t)s_e[qv[u]] * d + cv[u]) * I;
+            wv[u][0] = ld16_stream(wr + (size_t)ch0 * 8);
+            wv[u][1] = ld16_stream(wr + (size_t)ch1 * 8);
+        }
+#pragma unroll
+        for (int u = 0; u < IU; ++u) {
+            const int q = qv[u], c = cv[u];
+            float part = 0.f;
+            if (lane < nch) part = dot8_bf16(wv[u][0], hs[q * nch + lane], part);
+            if (lane + 64 < nch) part = dot8_bf16(wv[u][1], hs[q * nch + lane + 64], part);
+            // a row longer than 128 chunks: the rest, one piece at a time
+            const bf16_t *wr = Wdt + ((size_t)s_e[q] * d + c) * I;
+            for (int ch = lane + 128; ch < nch; ch += 64)
+                part = dot8_bf16(ld16_stream(wr + (size_t)ch * 8), hs[q * nch + ch], part);
+            const float o = wave_sum(part);
+            if (lane == 0 && i0 + u < n_items) so[q * per + (c - c_begin)] = o;
+        }
+    }
+    __syncthreads();
+    for (int cc = tid; cc < C; cc += 512) {
+        float acc = 0.f;
+        for (int q = 0; q < n; ++q) {
+            const float o = so[q * per + cc];
+            acc = q < S ? acc + o : fmaf(s_w[q], o, acc);
+        }
+        y[(size_t)t * d + c_begin + cc] = f32_to_bf16(acc);
+    }
+}
+
+hipError_t launch_down_small(const Plan &p, const void *W_dt, const Routing &r, const Work &w,
+                             void *y, hipStream_t s) {
+    // channel groups per token: about one workgroup per CU in all
+    int ng = device_cus() / p.T;
+    ng = ng < 1 ? 1 : ng;
+    const int per = (p.d + ng - 1) / ng;
+    const size_t lds = (size_t)(p.K + p.S) * p.I * 2 + (size_t)(p.K + p.S) * per * 4;
+    down_small<<<p.T * ng, 512, lds, s>>>(p.T, p.K, p.S, p.E, p.d, p.I, ng, r.masked_ids,
+                                          r.g_hat, w.pair_pos, (const bf16_t *)w.h,
+                                          (const bf16_t *)W_dt, (bf16_t *)y);
+    return hipGetLastError();
+}
+
 hipError_t launch_expert_up(const Plan &p, const void *x, const void *W_gu, const Routing &r,
                             const Work &w, hipStream_t s) {
     if (p.path == 1) return launch_tiled_up(p, x, W_gu, r, w, s);

@@ -6,6 +6,12 @@
 
 namespace beam {
 
+// decode batches of at most this many tokens take the small-batch kernels
+// (routing + up projection in one launch, down projection + combine in one)
+constexpr int SMALL_DECODE_T = 8;
+// slots per token the small-batch down kernel holds in LDS (K + S)
+constexpr int SMALL_SLOTS = 32;
+
 // Everything the launchers need, fixed on the host from the descriptor.
 struct Plan {
     int T, d, E, K, I;
@@ -26,6 +32,7 @@ struct Plan {
     int s_ts;           // tokens per select tile (64)
     int n_tiles;        // ceil(T / s_ts)
     int fuse_scatter;   // T <= 1024: the compaction workgroup also places the pairs
+    int small;          // bf16 decode batch of <= SMALL_DECODE_T tokens: up_small / down_small
     long long cap;          // sorted_pairs capacity
     long long n_blocks_cap; // block_expert capacity
     int max_active;     // host upper bound on experts with >= 1 active pair
@@ -58,7 +65,11 @@ struct Work {  // workspace views
     void *o;
 };
 
-// router logits, select and compaction
+// CUs of the current device (host; 256 when unknown)
+int device_cus();
+// router logits only (rows a1), and the logits plus select and compaction
+hipError_t launch_router_logits(const Plan &p, const void *x, const void *Wg, const void *Wm,
+                                const Routing &r, hipStream_t s);
 hipError_t launch_route(const Plan &p, const void *x, const void *Wg, const void *Wm,
                         const Routing &r, const Work &w, hipStream_t s);
 // pair scatter for large batches (no-op when the routing kernel placed them)
@@ -77,6 +88,12 @@ hipError_t launch_expert_down(const Plan &p, const void *W_dt, const Routing &r,
                               const Work &w, hipStream_t s);
 hipError_t launch_combine(const Plan &p, const Routing &r, const Work &w, void *y,
                           hipStream_t s);
+// small decode batches: routing + expert up projection; down projection +
+// combine (Plan::small)
+hipError_t launch_up_small(const Plan &p, const void *x, const void *W_gu, const Routing &r,
+                           const Work &w, hipStream_t s);
+hipError_t launch_down_small(const Plan &p, const void *W_dt, const Routing &r, const Work &w,
+                             void *y, hipStream_t s);
 // mask-router backward: workspace layout and launches
 struct BwdPlan {
     int T_pad, E_pad;       // tokens rounded up to the dW chunk, experts to 16

@@ -200,7 +200,7 @@ template <int EJ, int TB>
 __device__ __forceinline__ void select_group(
     int T, int E, int K, float thr, const Routing &r,
     std::conditional_t<TB == 64, unsigned long long, unsigned> *tmask, int *s_mid, int t_first,
-    int lane) {
+    int lane, bool write = true) {
     using MW = std::conditional_t<TB == 64, unsigned long long, unsigned>;
     static_assert(TB == 64 || TB == 16, "token bits per mask word");
     static_assert(EJ >= 1 && EJ <= 16, "at most 16 experts per lane (E <= 256)");
@@ -264,11 +264,13 @@ __device__ __forceinline__ void select_group(
     const float g = num / den;
     const bool m = z >= thr;
     const int o = t * K + k;
-    r.topk_ids[o] = mye;
-    r.topk_weights[o] = g;
-    r.mask[o] = m ? 1 : 0;
-    r.g_hat[o] = m ? g : 0.f;
-    r.masked_ids[o] = m ? mye : -1;
+    if (write) {
+        r.topk_ids[o] = mye;
+        r.topk_weights[o] = g;
+        r.mask[o] = m ? 1 : 0;
+        r.g_hat[o] = m ? g : 0.f;
+        r.masked_ids[o] = m ? mye : -1;
+    }
     if (s_mid) s_mid[o] = m ? mye : -1;
     if (m) atomicOr(&tmask[mye], (MW)1 << tl);
 }
@@ -332,9 +334,49 @@ __global__ __launch_bounds__(1024) void compact_tiles(const uint64_t *__restrict
                               s_part, s_cnt, s_off, s_words, s_tb);
 }
 
-// A small batch (T <= 64, one tile) in one workgroup: select, counts,
-// offsets, lists and pair positions of the E routed and S shared experts;
-// the token sets and masked ids stay in LDS.
+// The routing of a small batch (T <= 64, one tile) by one workgroup of
+// nthreads threads (>= 256, a multiple of 64): select, counts, offsets,
+// lists and pair positions of the E routed and S shared experts; the token
+// sets and masked ids stay in LDS.  write = false keeps every result in LDS
+// (token sets, masked ids, counts, offsets and, if given, the ascending
+// active-expert list) and writes nothing to global memory.
+template <int EJ>
+__device__ __forceinline__ void route_small_body(
+    int T, int E, int S, int K, float thr, int bm, const Routing &r, int32_t *pair_pos,
+    int32_t *meta, int32_t *sorted_tok, int32_t *pbt, int split, bool write, int tid, int nthreads,
+    unsigned long long *tmask, int *s_mid, int *s_cnt, int *s_off, int *s_act, int *s_nact) {
+    const int E2 = E + S;
+    if (tid < E) tmask[tid] = 0ull;
+    __syncthreads();
+    // four tokens per wave
+    for (int t_first = (tid >> 6) * 4; t_first < T; t_first += (nthreads >> 6) * 4)
+        select_group<EJ, 64>(T, E, K, thr, r, tmask, s_mid, t_first, tid & 63, write);
+    __syncthreads();
+    if (tid < E2) s_cnt[tid] = tid < E ? __popcll(tmask[tid]) : T;
+    __syncthreads();
+    if (tid < 64)
+        offsets_from_counts(s_cnt, s_off, E2, bm, r, meta, pbt, split, tid, write, s_act, s_nact);
+    __syncthreads();
+    if (!write) return;
+    const int TK = T * K, PT = TK + T * S;
+    blocks_and_pads(s_off, s_cnt, E2, bm, PT, r, sorted_tok, tid, nthreads);
+    for (int p = tid; p < TK; p += nthreads) {
+        const int e = s_mid[p];
+        if (e < 0) {
+            pair_pos[p] = -1;
+            continue;
+        }
+        const int t = p / K;
+        place_pair(p, t, s_off[e] + __popcll(tmask[e] & ((1ull << t) - 1ull)), r, pair_pos,
+                   sorted_tok);
+    }
+    for (int q = tid; q < T * S; q += nthreads) {  // shared experts: every token, in order
+        const int t = q / S, sx = q - t * S;
+        place_pair(TK + q, t, s_off[E + sx] + t, r, pair_pos, sorted_tok);
+    }
+}
+
+// A small batch (T <= 64, one tile) in one workgroup.
 template <int EJ>
 __global__ __launch_bounds__(1024) void route_small(int T, int E, int S, int K, float thr, int bm,
                                                     Routing r, int32_t *__restrict__ pair_pos,
@@ -345,34 +387,139 @@ __global__ __launch_bounds__(1024) void route_small(int T, int E, int S, int K, 
     __shared__ int s_mid[64 * 16];
     __shared__ int s_cnt[256];
     __shared__ int s_off[257];
+    route_small_body<EJ>(T, E, S, K, thr, bm, r, pair_pos, meta, sorted_tok, pbt, split, true,
+                         threadIdx.x, 1024, tmask, s_mid, s_cnt, s_off, nullptr, nullptr);
+}
+
+// ---------------------------------------------------------------------------
+// A decode batch of at most SMALL_DECODE_T tokens: the routing (rows a2-a4)
+// and the expert up projection (row a5) in one launch after the logits.
+// Every workgroup routes the batch itself from the logits (Top-K, mask,
+// counts, offsets and the active-expert list in LDS); workgroup 0 also
+// writes every routing output exactly as route_small does.  Then each wave
+// takes (active expert, intermediate unit j) items: it streams the gate row j
+// and the up row I + j of the expert (16-byte loads, lane l reading chunks
+// l, l + 64, ...), dots them with the x rows of the expert's tokens (staged
+// in LDS; bf16 pairs, float32 accumulation), sums the lanes in a fixed order
+// and writes h = SiLU(a) * u for each token at its sorted position.  With a
+// few tokens per expert the work is reading the active experts' rows, and
+// one item per wave at a time keeps every CU streaming (a projection of a
+// single token has 1536 such rows per expert).
+// ---------------------------------------------------------------------------
+template <int EJ>
+__global__ __launch_bounds__(512) void up_small(int T, int E, int S, int K, float thr, int bm,
+                                                int d, int I, Routing r,
+                                                int32_t *__restrict__ pair_pos,
+                                                int32_t *__restrict__ meta,
+                                                int32_t *__restrict__ sorted_tok,
+                                                int32_t *__restrict__ pbt, int split,
+                                                const bf16_t *__restrict__ x,
+                                                const bf16_t *__restrict__ Wgu,
+                                                bf16_t *__restrict__ h) {
+    __shared__ unsigned long long tmask[256];
+    __shared__ int s_mid[SMALL_DECODE_T * 16];
+    __shared__ int s_cnt[256];
+    __shared__ int s_off[257];
+    __shared__ int s_act[256];
+    __shared__ int s_nact;
+    extern __shared__ __align__(16) unsigned char xs_raw[];  // [T][d] bf16
+    u32x4 *xs = reinterpret_cast<u32x4 *>(xs_raw);
     const int tid = threadIdx.x;
-    const int E2 = E + S;
-    if (tid < E) tmask[tid] = 0ull;
-    __syncthreads();
-    // 16 waves of 4 tokens: one pass over a 64-token tile
-    const int t_first = (tid >> 6) * 4;
-    if (t_first < T) select_group<EJ, 64>(T, E, K, thr, r, tmask, s_mid, t_first, tid & 63);
-    __syncthreads();
-    if (tid < E2) s_cnt[tid] = tid < E ? __popcll(tmask[tid]) : T;
-    __syncthreads();
-    if (tid < 64) offsets_from_counts(s_cnt, s_off, E2, bm, r, meta, pbt, split, tid);
-    __syncthreads();
-    const int TK = T * K, PT = TK + T * S;
-    blocks_and_pads(s_off, s_cnt, E2, bm, PT, r, sorted_tok, tid, 1024);
-    for (int p = tid; p < TK; p += 1024) {
-        const int e = s_mid[p];
-        if (e < 0) {
-            pair_pos[p] = -1;
-            continue;
+    const int nch = d >> 3;  // 16-byte chunks per row
+    for (int i = tid; i < T * nch; i += 512) xs[i] = ld16(x + (size_t)i * 8);
+    route_small_body<EJ>(T, E, S, K, thr, bm, r, pair_pos, meta, sorted_tok, pbt, split,
+                         blockIdx.x == 0, tid, 512, tmask, s_mid, s_cnt, s_off, s_act, &s_nact);
+    const int lane = tid & 63;
+    const int n_items = s_nact * I;
+    const int waves = gridDim.x * 8;
+    // two items per wave at a time, both items' row pieces requested before
+    // any arithmetic
+    for (int it0 = blockIdx.x * 8 + (tid >> 6); it0 < n_items; it0 += 2 * waves) {
+        int e2[2], j2[2];
+        unsigned tm2[2];
+        bool ok[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int it = it0 + u * waves;
+            ok[u] = it < n_items;
+            const int itc = ok[u] ? it : it0;
+            const int a = itc / I;
+            j2[u] = itc - a * I;
+            e2[u] = s_act[a];
+            // tokens of this expert's active pairs (shared experts: every token)
+            tm2[u] = ok[u] ? (e2[u] < E ? (unsigned)tmask[e2[u]] : (1u << T) - 1u) : 0u;
         }
-        const int t = p / K;
-        place_pair(p, t, s_off[e] + __popcll(tmask[e] & ((1ull << t) - 1ull)), r, pair_pos,
-                   sorted_tok);
+        float ga[2][SMALL_DECODE_T], ua[2][SMALL_DECODE_T];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int t = 0; t < SMALL_DECODE_T; ++t) ga[u][t] = ua[u][t] = 0.f;
+        for (int c0 = 0; c0 < nch; c0 += 256) {
+            // every load is issued (past the row end: the row's first chunk
+            // again, in bounds and unused), so all of them stay in flight
+            u32x4 wgv[2][4], wuv[2][4];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const bf16_t *wg = Wgu + ((size_t)e2[u] * 2 * I + j2[u]) * d;
+                const bf16_t *wu = wg + (size_t)I * d;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int ch = c0 + lane + 64 * q;
+                    const int chc = ch < nch ? ch : 0;
+                    wgv[u][q] = ld16_stream(wg + (size_t)chc * 8);
+                    wuv[u][q] = ld16_stream(wu + (size_t)chc * 8);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+#pragma unroll
+                for (int t = 0; t < SMALL_DECODE_T; ++t) {
+                    if (!((tm2[u] >> t) & 1u)) continue;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int ch = c0 + lane + 64 * q;
+                        if (ch < nch) {
+                            const u32x4 xv = xs[t * nch + ch];
+                            ga[u][t] = dot8_bf16(wgv[u][q], xv, ga[u][t]);
+                            ua[u][t] = dot8_bf16(wuv[u][q], xv, ua[u][t]);
+                        }
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+            for (int t = 0; t < SMALL_DECODE_T; ++t) {
+                if (!((tm2[u] >> t) & 1u)) continue;
+                const float av = wave_sum(ga[u][t]);
+                const float uv = wave_sum(ua[u][t]);
+                if (lane == 0) {
+                    const int e = e2[u];
+                    const int pos = s_off[e] + (e < E ? __popc(tm2[u] & ((1u << t) - 1u)) : t);
+                    h[(size_t)pos * I + j2[u]] = f32_to_bf16(silu_fast(av) * uv);
+                }
+            }
+        }
     }
-    for (int q = tid; q < T * S; q += 1024) {  // shared experts: every token, in order
-        const int t = q / S, sx = q - t * S;
-        place_pair(TK + q, t, s_off[E + sx] + t, r, pair_pos, sorted_tok);
-    }
+}
+
+hipError_t launch_up_small(const Plan &p, const void *x, const void *W_gu, const Routing &r,
+                           const Work &w, hipStream_t s) {
+    const int ej = (p.E + 15) / 16;
+    const size_t lds = (size_t)p.T * p.d * 2;
+    const int grid = device_cus();
+#define BEAM_UP_SMALL(EJV)                                                                     \
+    up_small<EJV><<<grid, 512, lds, s>>>(p.T, p.E, p.S, p.K, p.thr, p.bm, p.d, p.I, r,        \
+                                         w.pair_pos, w.meta, w.sorted_tok, w.pbt, p.split,   \
+                                         (const bf16_t *)x, (const bf16_t *)W_gu, (bf16_t *)w.h)
+    if (ej <= 1) BEAM_UP_SMALL(1);
+    else if (ej <= 2) BEAM_UP_SMALL(2);
+    else if (ej <= 4) BEAM_UP_SMALL(4);
+    else if (ej <= 8) BEAM_UP_SMALL(8);
+    else BEAM_UP_SMALL(16);
+#undef BEAM_UP_SMALL
+    return hipGetLastError();
 }
 
 // A batch of at most BEAM_SMALL_T tokens (one 64-token tile) is routed by
@@ -425,8 +572,8 @@ static void launch_select(const Plan &p, const Routing &r, const Work &w, hipStr
 #define BEAM_ROUTER_WIDE_T 1024
 #endif
 
-hipError_t launch_route(const Plan &p, const void *x, const void *Wg, const void *Wm,
-                        const Routing &r, const Work &w, hipStream_t s) {
+hipError_t launch_router_logits(const Plan &p, const void *x, const void *Wg, const void *Wm,
+                                const Routing &r, hipStream_t s) {
     if (p.dtype == 1 && p.path == 1 && p.T > BEAM_ROUTER_GEMM_T) {
         // large batch: the logits as one dense MFMA GEMM
         hipError_t err = launch_gemm_router(p, x, Wg, Wm, r, s);
@@ -466,7 +613,12 @@ hipError_t launch_route(const Plan &p, const void *x, const void *Wg, const void
             (const float *)x, (const float *)Wg, (const float *)Wm, r.gate_logits, r.mask_logits,
             p.T, p.d, p.E);
     }
-    hipError_t err = hipGetLastError();
+    return hipGetLastError();
+}
+
+hipError_t launch_route(const Plan &p, const void *x, const void *Wg, const void *Wm,
+                        const Routing &r, const Work &w, hipStream_t s) {
+    const hipError_t err = launch_router_logits(p, x, Wg, Wm, r, s);
     if (err != hipSuccess) return err;
     launch_select(p, r, w, s);
     return hipGetLastError();
