@@ -257,38 +257,53 @@ __global__ __launch_bounds__(512) void down_small(int T, int K, int S, int E, in
     __syncthreads();
     const int n = s_n;
     const int nch = I >> 3;  // 16-byte chunks per row
-    for (int i = tid; i < n * nch; i += 512) {
-        const int q = i / nch, ch = i - q * nch;
-        hs[i] = ld16(h + (size_t)s_pos[q] * I + (size_t)ch * 8);
-    }
-    __syncthreads();
     const int c_begin = grp * per, c_end = min(d, c_begin + per);
     const int C = c_end > c_begin ? c_end - c_begin : 0;
     const int n_items = n * C;
     constexpr int IU = 8;  // items per wave at a time
     // every load is issued (past the end: item i0 / the row's first chunk
     // again, in bounds and unused), so the compiler keeps all of them in
-    // flight
+    // flight; a batch's rows are requested before the previous batch's
+    // arithmetic (the first batch before the h rows are staged)
     const int ch0 = lane < nch ? lane : 0;
     const int ch1 = lane + 64 < nch ? lane + 64 : 0;
-    for (int i0 = wave * IU; i0 < n_items; i0 += 8 * IU) {
-        u32x4 wv[IU][2];
-        int qv[IU], cv[IU];
+    u32x4 wv[IU][2];
+    int qv[IU], cv[IU];
+    auto request = [&](int i0) {
 #pragma unroll
         for (int u = 0; u < IU; ++u) {
-            const int it = i0 + u < n_items ? i0 + u : i0;
-            qv[u] = it / C;
+            const int it = i0 + u < n_items ? i0 + u : (i0 < n_items ? i0 : 0);
+            qv[u] = C > 0 ? it / C : 0;
             cv[u] = c_begin + (it - qv[u] * C);
-            const bf16_t *wr = Wdt + ((size_t)s_e[qv[u]] * d + cv[u]) * I;
+            const bf16_t *wr = Wdt + ((size_t)s_e[qv[u]] * d + (cv[u] < d ? cv[u] : 0)) * I;
             wv[u][0] = ld16_stream(wr + (size_t)ch0 * 8);
             wv[u][1] = ld16_stream(wr + (size_t)ch1 * 8);
         }
+    };
+    int i0 = wave * IU;
+    if (i0 < n_items) request(i0);
+    for (int i = tid; i < n * nch; i += 512) {
+        const int q = i / nch, ch = i - q * nch;
+        hs[i] = ld16(h + (size_t)s_pos[q] * I + (size_t)ch * 8);
+    }
+    __syncthreads();
+    for (; i0 < n_items; i0 += 8 * IU) {
+        u32x4 cur[IU][2];
+        int qc[IU], cc_[IU];
 #pragma unroll
         for (int u = 0; u < IU; ++u) {
-            const int q = qv[u], c = cv[u];
+            cur[u][0] = wv[u][0];
+            cur[u][1] = wv[u][1];
+            qc[u] = qv[u];
+            cc_[u] = cv[u];
+        }
+        if (i0 + 8 * IU < n_items) request(i0 + 8 * IU);
+#pragma unroll
+        for (int u = 0; u < IU; ++u) {
+            const int q = qc[u], c = cc_[u];
             float part = 0.f;
-            if (lane < nch) part = dot8_bf16(wv[u][0], hs[q * nch + lane], part);
-            if (lane + 64 < nch) part = dot8_bf16(wv[u][1], hs[q * nch + lane + 64], part);
+            if (lane < nch) part = dot8_bf16(cur[u][0], hs[q * nch + lane], part);
+            if (lane + 64 < nch) part = dot8_bf16(cur[u][1], hs[q * nch + lane + 64], part);
             // a row longer than 128 chunks: the rest, one piece at a time
             const bf16_t *wr = Wdt + ((size_t)s_e[q] * d + c) * I;
             for (int ch = lane + 128; ch < nch; ch += 64)

@@ -114,6 +114,52 @@ __global__ __launch_bounds__(NW * 64) void router_logits_bf16(
     }
 }
 
+// Router logits of a decode batch of at most SMALL_DECODE_T tokens (bf16):
+// one wave per logit column (row n of W_gate, or of W_mask for n >= E), all
+// of its weight row and the batch's x rows requested at once (16-byte loads,
+// lane l reading chunks l, l + 64, ...), bf16 dot products with float32
+// accumulation, lanes summed in a fixed order.  Every column's bytes are
+// read in one round trip, where the MFMA kernel's 16-column blocks leave
+// most CUs idle for a batch this small.
+__global__ __launch_bounds__(256) void router_logits_small(
+    const bf16_t *__restrict__ x, const bf16_t *__restrict__ Wg, const bf16_t *__restrict__ Wm,
+    float *__restrict__ gate_logits, float *__restrict__ mask_logits, int T, int d, int E) {
+    const int lane = threadIdx.x & 63;
+    const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (n >= 2 * E) return;
+    const bf16_t *w = n < E ? Wg + (size_t)n * d : Wm + (size_t)(n - E) * d;
+    const int nch = d >> 3;
+    float acc[SMALL_DECODE_T];
+#pragma unroll
+    for (int t = 0; t < SMALL_DECODE_T; ++t) acc[t] = 0.f;
+    for (int c0 = 0; c0 < nch; c0 += 256) {
+        u32x4 wv[4], xv[SMALL_DECODE_T][4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int ch = c0 + lane + 64 * q;
+            const int chc = ch < nch ? ch : 0;
+            wv[q] = ld16(w + (size_t)chc * 8);
+#pragma unroll
+            for (int t = 0; t < SMALL_DECODE_T; ++t)
+                if (t < T) xv[t][q] = ld16(x + (size_t)t * d + (size_t)chc * 8);
+        }
+#pragma unroll
+        for (int t = 0; t < SMALL_DECODE_T; ++t) {
+            if (t >= T) break;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (c0 + lane + 64 * q < nch) acc[t] = dot8_bf16(wv[q], xv[t][q], acc[t]);
+        }
+    }
+    float *out = n < E ? gate_logits + n : mask_logits + (n - E);
+#pragma unroll
+    for (int t = 0; t < SMALL_DECODE_T; ++t) {
+        if (t >= T) break;
+        const float v = wave_sum(acc[t]);
+        if (lane == 0) out[(size_t)t * E] = v;
+    }
+}
+
 // Router logits, float32 layer: plain float dot products, one thread per
 // (token, column).
 template <typename T_>
@@ -426,9 +472,23 @@ __global__ __launch_bounds__(512) void up_small(int T, int E, int S, int K, floa
     u32x4 *xs = reinterpret_cast<u32x4 *>(xs_raw);
     const int tid = threadIdx.x;
     const int nch = d >> 3;  // 16-byte chunks per row
-    for (int i = tid; i < T * nch; i += 512) xs[i] = ld16(x + (size_t)i * 8);
+    // the batch's x rows: requested before the routing, stored to LDS after
+    // it (T * d * 2 <= 48 KB: at most 6 chunks per thread)
+    constexpr int XR = 6;
+    u32x4 xr[XR];
+#pragma unroll
+    for (int k = 0; k < XR; ++k) {
+        const int i = tid + 512 * k;
+        if (i < T * nch) xr[k] = ld16(x + (size_t)i * 8);
+    }
     route_small_body<EJ>(T, E, S, K, thr, bm, r, pair_pos, meta, sorted_tok, pbt, split,
                          blockIdx.x == 0, tid, 512, tmask, s_mid, s_cnt, s_off, s_act, &s_nact);
+#pragma unroll
+    for (int k = 0; k < XR; ++k) {
+        const int i = tid + 512 * k;
+        if (i < T * nch) xs[i] = xr[k];
+    }
+    __syncthreads();
     const int lane = tid & 63;
     const int n_items = s_nact * I;
     const int waves = gridDim.x * 8;
@@ -578,6 +638,10 @@ hipError_t launch_router_logits(const Plan &p, const void *x, const void *Wg, co
         // large batch: the logits as one dense MFMA GEMM
         hipError_t err = launch_gemm_router(p, x, Wg, Wm, r, s);
         if (err != hipSuccess) return err;
+    } else if (p.small) {
+        router_logits_small<<<(2 * p.E + 3) / 4, 256, 0, s>>>(
+            (const bf16_t *)x, (const bf16_t *)Wg, (const bf16_t *)Wm, r.gate_logits,
+            r.mask_logits, p.T, p.d, p.E);
     } else if (p.dtype == 1) {
         // up to a few hundred tokens: 16-token tiles of one column block (the
         // most workgroups, the fewest bytes per workgroup); more: 32-token
