@@ -491,10 +491,14 @@ __global__ __launch_bounds__(512) void up_small(int T, int E, int S, int K, floa
     __syncthreads();
     const int lane = tid & 63;
     const int n_items = s_nact * I;
-    const int waves = gridDim.x * 8;
+    // workgroup 0 writes the routing outputs; the others take the items, so
+    // its writes overlap their streaming (with one workgroup it takes them)
+    const int g0 = gridDim.x > 1 ? 1 : 0;
+    if (blockIdx.x < g0) return;
+    const int waves = (gridDim.x - g0) * 8;
     // two items per wave at a time, both items' row pieces requested before
     // any arithmetic
-    for (int it0 = blockIdx.x * 8 + (tid >> 6); it0 < n_items; it0 += 2 * waves) {
+    for (int it0 = (blockIdx.x - g0) * 8 + (tid >> 6); it0 < n_items; it0 += 2 * waves) {
         int e2[2], j2[2];
         unsigned tm2[2];
         bool ok[2];
