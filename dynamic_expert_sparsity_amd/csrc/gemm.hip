@@ -1,6 +1,6 @@
-// Launchers of the grouped GEMM (kernels in gemm_dev.h) and of the tiled
-// path's expert kernel, which runs one of the three kernel families the
-// compaction picked for the call (ring_dev.h, gemm_dev.h).
+// The tiled path's expert kernel and its launchers: one launch per
+// projection runs the kernel family the compaction picked for the call (the
+// streaming bodies of ring_dev.h or the grouped GEMM of gemm_dev.h).
 #include <mutex>
 
 #include "gemm_dev.h"
@@ -19,20 +19,6 @@ static int persistent_wgs() {
         n = n >= 8 ? n / 8 * 8 : 256;
     });
     return n;
-}
-
-template <int MODE, int BM, int NA, int NB, int DKK, int WT>
-static hipError_t launch_gemm(const GemmArgs &a, hipStream_t s) {
-    static std::once_flag once;
-    static hipError_t attr_err = hipSuccess;
-    using C = GemmCfg<BM, NA, NB, DKK, WT>;
-    std::call_once(once, [] {
-        attr_err = hipFuncSetAttribute((const void *)grouped_gemm<MODE, BM, NA, NB, DKK, WT>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-    });
-    if (attr_err != hipSuccess) return attr_err;
-    grouped_gemm<MODE, BM, NA, NB, DKK, WT><<<persistent_wgs(), C::NW * 64, C::LDS_BYTES, s>>>(a);
-    return hipGetLastError();
 }
 
 static GemmArgs base_args(const Plan &p, const Routing &r, const Work &w) {
@@ -126,23 +112,6 @@ hipError_t launch_tiled_down(const Plan &p, const void *W_dt, const Routing &r, 
                      (bf16_t *)w.o, p.I, p.d};
     return p.I % 256 == 0 ? launch_tiled_t<true, false>(a, q, s)
                           : launch_tiled_t<true, true>(a, q, s);
-}
-
-hipError_t launch_gemm_router(const Plan &p, const void *x, const void *Wg, const void *Wm,
-                              const Routing &r, hipStream_t s) {
-    GemmArgs a{};
-    a.A = (const bf16_t *)x;
-    a.a_bytes = 0;  // the router's operands go through pointers
-    a.W = (const bf16_t *)Wg;
-    a.W2 = (const bf16_t *)Wm;
-    a.gate_logits = r.gate_logits;
-    a.mask_logits = r.mask_logits;
-    a.T = p.T;
-    a.d = p.d;
-    a.E = p.E;
-    a.n_ntiles = (2 * p.E + GBN - 1) / GBN;
-    a.n_rblocks = (p.T + GBM_R - 1) / GBM_R;
-    return launch_gemm<MODE_ROUTER, GBM_R, 3, 3, 3, 64>(a, s);
 }
 
 }  // namespace beam

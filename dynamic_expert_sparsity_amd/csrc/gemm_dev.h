@@ -1,30 +1,27 @@
-// a5-a6 (and a1 for large batches): the SwiGLU experts (BEAM paper, section
-// 3.1 Eq. 3) as a grouped bf16 GEMM over the block-padded per-expert lists,
-// on the v_mfma_f32_32x32x16_bf16 matrix cores.  Only experts with active
-// pairs have blocks, so masked pairs cost no FLOPs and their experts no bytes.
-// The same kernel, in ROUTER mode, computes the two routers' logits (Eq. 4-5)
-// of a large batch as one dense GEMM with 2E = 256 columns.
+// a5-a6: the SwiGLU experts (BEAM paper, section 3.1 Eq. 3) as a grouped
+// bf16 GEMM over the block-padded per-expert lists, on the
+// v_mfma_f32_32x32x16_bf16 matrix cores.  Only experts with active pairs
+// have blocks, so masked pairs cost no FLOPs and their experts no bytes.
 //
-// Tile: BM rows (UP/DOWN: one 128-position block of one expert, or 256
-// positions = up to two such blocks of one expert; ROUTER: 128 tokens) x 256
-// output columns, k in stages of 64.  The call's record says which height
+// Tile: BM rows (one 128-position block of one expert, or 256 positions =
+// up to two such blocks of one expert) x 256 output columns, k in stages of
+// 64.  The call's record says which height
 // works: a weight slice is read once per tile, so 256-row tiles halve the
 // weight reads of experts with many pairs, 128-row tiles waste fewer rows on
 // experts with few.  (BM / WT) (rows) x 2 (columns) waves, each WT x 128
-// (WT / 32 x 4 MFMA tiles of 32 x 32; WT = 64 for the 256-row and router
-// tiles, 32 for the 128-row expert tiles); a wave whose WT rows are all
+// (WT / 32 x 4 MFMA tiles of 32 x 32; WT = 64 for the 256-row tiles, 32 for
+// the 128-row tiles); a wave whose WT rows are all
 // padding of its expert's last block (or past the last token) skips its LDS
 // reads and MFMAs, and rows past the expert's segment are never stored.  UP: the 256
 // columns are 128 gate rows and the 128 matching up rows of W_gu, so each
 // wave holds gate and up accumulators of the same (position, unit) and
 // applies SiLU(a) * u in registers.  DOWN: A is h (contiguous rows), B is
-// W_dt.  ROUTER: A is x, B is W_gate then W_mask, fp32 out.
+// W_dt.
 //
 // Operands go from global memory straight into LDS (global_load_lds_dwordx4):
 // A (32 KB per stage) in a ring of two stages, B (32 KB) in a ring of three,
-// so the weights stream two stages ahead (160 KB of LDS; the router tiles use
-// three-stage rings of 16 + 32 KB).  Every row segment a load instruction fetches is a whole
-// 128-byte line (k = 64 bf16): a wave instruction fills 1 KB = 8 rows, lane l
+// so the weights stream two stages ahead (160 KB of LDS).  Every row
+// segment a load instruction fetches is a whole 128-byte line (k = 64 bf16): a wave instruction fills 1 KB = 8 rows, lane l
 // fetching chunk (l % 8) ^ f(row) of row l / 8; half-line segments would halve
 // the rate at which a CU can pull lines from L2.  LDS layout of a stage: row r
 // holds its 64 k-values as eight 16-byte chunks, chunk c at slot c ^ f(r) (see
@@ -53,7 +50,6 @@
 namespace beam {
 
 constexpr int GBM = 256;   // rows of the taller expert tile (two 128-row blocks of one expert)
-constexpr int GBM_R = 128; // rows per router tile (more tiles for a 2E-column GEMM)
 constexpr int GBN = 256;   // output columns per tile
 constexpr int GBK = 64;    // k per stage: one 128-byte line per row
 constexpr int G_ROWB = GBK * 2;       // bytes per row per stage
@@ -122,7 +118,7 @@ struct GemmCfg {
     static constexpr int ST_DOWN = MF * 16 * 4;
 };
 
-enum GemmMode { MODE_UP = 0, MODE_DOWN = 1, MODE_ROUTER = 2 };
+enum GemmMode { MODE_UP = 0, MODE_DOWN = 1 };
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
@@ -175,17 +171,14 @@ __device__ __forceinline__ void lds_dma16_buf(rsrc_t r, uint32_t voff, uint32_t 
 }
 
 struct GemmArgs {
-    const bf16_t *A;        // x (UP, ROUTER) or h (DOWN)
-    const bf16_t *W;        // W_gu (UP), W_dt (DOWN), W_gate (ROUTER)
-    const bf16_t *W2;       // W_mask (ROUTER)
+    const bf16_t *A;        // x (UP) or h (DOWN)
+    const bf16_t *W;        // W_gu (UP) or W_dt (DOWN)
     const int32_t *block_expert, *num_active, *sorted_tok;
     const int32_t *expert_offsets, *expert_counts;
     bf16_t *out;            // h (UP) or o (DOWN)
-    float *gate_logits, *mask_logits;  // ROUTER
     int T, d, I, E;
     uint32_t a_bytes;       // bytes of A (UP: x, DOWN: h; below 2^31)
     int n_ntiles;           // column tiles per block
-    int n_rblocks;          // ROUTER: row blocks
     const int32_t *mode;    // UP/DOWN: the call's record {family, max count, records, 0}
     const int32_t *pbt;     // UP/DOWN, 256-row tiles: {expert, first position, segment rows,
                             // valid rows} per tile
@@ -210,8 +203,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
     const int lh = lane >> 5;
 
     // the call's kernel family: 1 = 128-row tiles, 2 = 256-row tiles (0 = streaming)
-    if (MODE != MODE_ROUTER && g.mode[0] != (BM == 256 ? 2 : 1)) return;
-    const int n_blocks = MODE == MODE_ROUTER ? g.n_rblocks : BM == 256 ? g.mode[2] : g.num_active[3];
+    if (g.mode[0] != (BM == 256 ? 2 : 1)) return;
+    const int n_blocks = BM == 256 ? g.mode[2] : g.num_active[3];
     const int n_tiles = n_blocks * g.n_ntiles;
     const int xcd = blockIdx.x & 7;
     const int per_xcd_wg = gridDim.x >> 3;
@@ -237,17 +230,15 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
         for (int n = 0; n < 4; ++n) brow[n] = wn * 128 + n * 32;
     }
 
-    // One tile's place in the problem and its operand addresses.  UP/DOWN
-    // address their operands through buffer resources (32-bit byte offsets
-    // per lane; the stage's k offset goes in the scalar offset), the router
-    // through pointers.
+    // One tile's place in the problem and its operand addresses, which go
+    // through buffer resources (32-bit byte offsets per lane; the stage's k
+    // offset goes in the scalar offset).
     struct Tile {
         int pos0, nt, seg, rows_valid;
         bool live;
         unsigned a_send;   // bit u: A load u has a valid row (wave-uniform)
-        rsrc_t rB;         // UP/DOWN: the expert's weights
+        rsrc_t rB;         // the expert's weights
         uint32_t offA[C::LA], offB[C::LB];
-        const bf16_t *srcA[MODE == MODE_ROUTER ? C::LA : 1], *srcB[MODE == MODE_ROUTER ? C::LB : 1];
     };
     const rsrc_t rA = make_rsrc(g.A, g.a_bytes);
     // A loads whose 8 rows all lie past the tile's valid rows are not
@@ -257,21 +248,16 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
     // wait allows only B loads to be outstanding, which are always sent
     // (so a missing A load never shortens a wait).  Keeps the weight
     // stream and drops the DMA of a part-filled tile's empty rows.
-    constexpr bool SKIP_A = G_SKIP_A && MODE != MODE_ROUTER && NB == NA + 1;
+    constexpr bool SKIP_A = G_SKIP_A && NB == NA + 1;
 
     auto setup = [&](int tile, Tile &t) {
         const int blk = tile / g.n_ntiles;
         t.nt = tile - blk * g.n_ntiles;
         // tile: BM rows from pos0 of expert e; seg of them lie in the expert's
         // padded segment (a 256-row tile can end after 128), rows_valid hold
-        // real pairs (tokens, for the router)
+        // real pairs
         int e;
-        if (MODE == MODE_ROUTER) {
-            t.pos0 = blk * BM;
-            e = 0;
-            t.seg = BM;
-            t.rows_valid = g.T - t.pos0;
-        } else if (BM == 256) {
+        if (BM == 256) {
             const int4 rec = *reinterpret_cast<const int4 *>(g.pbt + 4 * blk);
             e = rec.x;
             t.pos0 = rec.y;
@@ -284,10 +270,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
             t.rows_valid = g.expert_offsets[e] + g.expert_counts[e] - t.pos0;
         }
         t.live = __builtin_amdgcn_readfirstlane(wm * WT < t.rows_valid ? 1 : 0) != 0;
-        if (MODE != MODE_ROUTER) {
-            const size_t wrows = MODE == MODE_UP ? (size_t)2 * g.I : (size_t)g.d;
-            t.rB = make_rsrc(g.W + (size_t)e * wrows * ldw, (uint32_t)(wrows * ldw * 2));
-        }
+        const size_t wrows = MODE == MODE_UP ? (size_t)2 * g.I : (size_t)g.d;
+        t.rB = make_rsrc(g.W + (size_t)e * wrows * ldw, (uint32_t)(wrows * ldw * 2));
         // this lane's 16 bytes land at slot l % 8 of row r: chunk (l % 8) ^ f(r)
 #pragma unroll
         for (int i = 0; i < C::LA; ++i) {
@@ -296,14 +280,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
             // read the segment's first row; nothing stores them
             const int rs = r < t.seg ? r : 0;
             const int ch = ((lane & 7) ^ swz_f(r)) * 8;
-            if (MODE == MODE_UP) {
+            if (MODE == MODE_UP)
                 t.offA[i] = ((uint32_t)g.sorted_tok[t.pos0 + rs] * (uint32_t)g.d + ch) * 2u;
-            } else if (MODE == MODE_DOWN) {
+            else
                 t.offA[i] = ((uint32_t)(t.pos0 + rs) * (uint32_t)g.I + ch) * 2u;
-            } else {
-                const int tk = min(t.pos0 + r, g.T - 1);
-                t.srcA[i] = g.A + (size_t)tk * g.d + ch;
-            }
         }
 #pragma unroll
         for (int i = 0; i < C::LB; ++i) {
@@ -312,11 +292,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
             if (MODE == MODE_UP) {
                 const int wr = r < 128 ? t.nt * 128 + r : g.I + t.nt * 128 + (r - 128);
                 t.offB[i] = ((uint32_t)wr * (uint32_t)ldw + ch) * 2u;
-            } else if (MODE == MODE_DOWN) {
-                t.offB[i] = ((uint32_t)(t.nt * GBN + r) * (uint32_t)ldw + ch) * 2u;
             } else {
-                const int n = min(t.nt * GBN + r, 2 * g.E - 1);
-                t.srcB[i] = (n < g.E ? g.W + (size_t)n * ldw : g.W2 + (size_t)(n - g.E) * ldw) + ch;
+                t.offB[i] = ((uint32_t)(t.nt * GBN + r) * (uint32_t)ldw + ch) * 2u;
             }
         }
         t.a_send = 0;
@@ -333,8 +310,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
             const int j = p + NA - 1;
             if (j >= 0 && j < nst && ((t.a_send >> u) & 1u)) {
                 unsigned char *dst = lds + (j % NA) * C::A_BYTES + (wave + C::NW * u) * 1024;
-                if constexpr (MODE == MODE_ROUTER) lds_dma16(t.srcA[u] + j * GBK, dst);
-                else lds_dma16_buf(rA, t.offA[u], (uint32_t)j * G_ROWB, dst);
+                lds_dma16_buf(rA, t.offA[u], (uint32_t)j * G_ROWB, dst);
             }
         } else {
             const int j = p + NB - 1;
@@ -345,8 +321,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
                 // a weight slice is then read by one tile only and streams
                 // past the L2 (non-temporal); the 256-row tiles of an expert
                 // with several of them share its slices through the L2
-                if constexpr (MODE == MODE_ROUTER) lds_dma16(t.srcB[u - C::LA] + j * GBK, dst);
-                else lds_dma16_buf<BM == 128 ? 2 : 0>(t.rB, t.offB[u - C::LA], (uint32_t)j * G_ROWB, dst);
+                lds_dma16_buf<BM == 128 ? 2 : 0>(t.rB, t.offB[u - C::LA], (uint32_t)j * G_ROWB, dst);
             }
         }
     };
@@ -402,9 +377,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
             // every prologue load is older than the stores: all of them done
             // once at most min(stores, 63) operations are in flight, which
             // also lets the newest stage's B loads finish (a stricter wait)
-            if constexpr (MODE == MODE_ROUTER) wait_vmcnt<0>();
-            else wait_vmcnt<(MODE == MODE_UP ? C::ST_UP : C::ST_DOWN) < 63
-                                 ? (MODE == MODE_UP ? C::ST_UP : C::ST_DOWN) : 63>();
+            wait_vmcnt<(MODE == MODE_UP ? C::ST_UP : C::ST_DOWN) < 63
+                           ? (MODE == MODE_UP ? C::ST_UP : C::ST_DOWN) : 63>();
         } else if (1 < nst) {
             wait_vmcnt<C::S_PRO>();
         } else {
@@ -448,7 +422,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
     // multiples of 128 rows, wave rows WT <= 64 aligned), so each wave
     // issues all of its C::ST stores or none.
     auto epilogue = [&](const Tile &t) {
-        if (MODE != MODE_ROUTER && wm * WT >= t.seg) return;  // the next expert's rows
+        if (wm * WT >= t.seg) return;  // the next expert's rows
 #pragma unroll
         for (int m = 0; m < MF; ++m) {
 #pragma unroll
@@ -462,20 +436,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
                         g.out[prow * g.I + j] =
                             f32_to_bf16(silu_fast(acc[m][n][v]) * acc[m][n + 2][v]);
                     }
-                } else if (MODE == MODE_DOWN) {
+                } else {
 #pragma unroll
                     for (int n = 0; n < 4; ++n) {
                         const int c = t.nt * GBN + wn * 128 + n * 32 + lr;
                         g.out[prow * g.d + c] = f32_to_bf16(acc[m][n][v]);
-                    }
-                } else {
-                    if ((int)prow < g.T) {
-#pragma unroll
-                        for (int n = 0; n < 4; ++n) {
-                            const int c = t.nt * GBN + wn * 128 + n * 32 + lr;
-                            if (c < g.E) g.gate_logits[prow * g.E + c] = acc[m][n][v];
-                            else if (c < 2 * g.E) g.mask_logits[prow * g.E + (c - g.E)] = acc[m][n][v];
-                        }
                     }
                 }
             }
@@ -513,15 +478,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
         }
         epilogue(cur);
         if (!more) break;
-        stores = MODE != MODE_ROUTER && wm * WT >= cur.seg ? 0 : 1;
+        stores = wm * WT >= cur.seg ? 0 : 1;
         cur = nxt;
         tile = next;
     }
-}
-
-template <int MODE, int BM, int NA, int NB, int DKK, int WT>
-__global__ __launch_bounds__(BM / WT * 128, 1) void grouped_gemm(GemmArgs g) {
-    gemm_body<MODE, BM, NA, NB, DKK, WT>(g);
 }
 
 }  // namespace beam

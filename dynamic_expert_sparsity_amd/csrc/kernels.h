@@ -80,8 +80,6 @@ hipError_t launch_tiled_up(const Plan &p, const void *x, const void *W_gu, const
                            const Work &w, hipStream_t s);
 hipError_t launch_tiled_down(const Plan &p, const void *W_dt, const Routing &r, const Work &w,
                              hipStream_t s);
-hipError_t launch_gemm_router(const Plan &p, const void *x, const void *Wg, const void *Wm,
-                              const Routing &r, hipStream_t s);
 hipError_t launch_expert_up(const Plan &p, const void *x, const void *W_gu, const Routing &r,
                             const Work &w, hipStream_t s);
 hipError_t launch_expert_down(const Plan &p, const void *W_dt, const Routing &r,

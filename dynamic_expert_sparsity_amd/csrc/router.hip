@@ -12,104 +12,167 @@
 // one workgroup that selects and groups a small batch, or one workgroup per
 // quarter of a 64-token tile for the select and one workgroup for the
 // grouping.
+#include <mutex>
 #include <type_traits>
 
 #include "compact_dev.h"
+#include "gemm_dev.h"
 
 namespace beam {
 
 // ---------------------------------------------------------------------------
-// Router logits block, bf16, MFMA 16x16x32.  The two routers are one GEMM
-// with 2E output columns: column n < E is W_gate row n, column E + n is
-// W_mask row n.  A workgroup owns 16*NC columns and 16*MT tokens; its NW
-// waves split d (every wave requests a batch of its x and weight fragments
-// before the MFMAs that use them) and their partial sums meet in LDS, where
-// wave c adds them for column block c in wave order and writes the finished
-// float32 logits.  A (x rows) and B (weight rows) are both k-contiguous, so
-// every lane's 16-byte load lands directly in MFMA layout.  More column
-// blocks per workgroup read each x row fewer times (2E / (16 NC) times in
-// all); one block gives the most workgroups for small batches.  Out-of-range
-// tokens / columns load a clamped row and their results are not stored.
+// Router logits block, bf16, MFMA 16x16x32.  The two routers are one GEMM with
+// 2E output columns: column n < E is W_gate row n, column E + n is W_mask row
+// n.  A workgroup owns 16*MT tokens and 16*NC columns of one of the two routers
+// (each router's columns are tiled on their own, so a workgroup's weight rows
+// all lie in one matrix and one buffer resource covers them).  Its NW waves
+// split d into contiguous runs of 64-wide k-chunks, and every wave streams its
+// run through a private ring of DEPTH LDS buffers: a chunk is the tile's x
+// rows and weight rows, 128 bytes (one cache line) of each, moved by
+// global_load_lds where every group of four lanes fetches one aligned 64-byte
+// piece.  (Loading MFMA fragments straight into registers puts sixteen
+// different rows in each load instruction, four lines per group of four lanes,
+// and the address unit then needs about four times as many cycles for the same
+// bytes.)  16-byte piece c of buffer row r sits at slot c ^ f(r) (f as in the
+// GEMM), so the sixteen rows of a fragment read fall in distinct banks.  A wave's chunks land in
+// order and it waits for each with an explicit vmcnt (the loads into its own
+// ring are its only vector memory operations), so no barrier is needed until
+// the partial sums meet in LDS, where wave c adds them for column blocks c, c
+// + NW, ... in wave order and writes the float32 logits.  More column blocks
+// per workgroup read each x row fewer times (2 ceil(E / 16 NC) times in all);
+// one block gives the most workgroups for small batches.  Out-of-range tokens /
+// columns load a clamped row and their results are not stored.
 // ---------------------------------------------------------------------------
-template <int MT, int NW, int NC>
+template <int MT, int NW, int NC, int DEPTH>
+struct RouterCfg {
+    static constexpr int ROWS = (MT + NC) * 16;  // buffer rows: x rows, then weight rows
+    static constexpr int BUF = ROWS * G_ROWB;    // one 64-wide k-chunk of them
+    static constexpr int LOADS = ROWS / G_RPI;   // 1 KB wave loads per chunk
+    static constexpr int WREG = DEPTH * BUF;     // a wave's ring
+    static constexpr int PART = MT * NC * 1024;  // a wave's partial sums
+    // partials in the wave's own ring when they fit (no barrier first), else
+    // in a region of their own after every wave is done with its ring
+    static constexpr bool OWN = PART <= WREG;
+    static constexpr int PSTRIDE = OWN ? WREG : PART;
+    static constexpr int LDS = NW * (OWN ? WREG : PART);
+    static_assert(OWN || PART >= WREG, "one layout for the LDS");
+    static_assert((DEPTH - 1) * LOADS < 64, "vmcnt range");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+// wait until at most `ahead` chunks of STEP loads each are in flight
+// (ahead <= N, wave-uniform)
+template <int N, int STEP>
+__device__ __forceinline__ void router_wait_chunks(int ahead) {
+    if constexpr (N == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (ahead >= N) wait_vmcnt<N * STEP>();
+        else router_wait_chunks<N - 1, STEP>(ahead);
+    }
+}
+
+template <int MT, int NW, int NC, int DEPTH>
 __global__ __launch_bounds__(NW * 64) void router_logits_bf16(
     const bf16_t *__restrict__ x, const bf16_t *__restrict__ Wg, const bf16_t *__restrict__ Wm,
     float *__restrict__ gate_logits, float *__restrict__ mask_logits, int T, int d, int E) {
-    static_assert(NC <= NW, "one wave per column block in the final sum");
-    __shared__ f32x4 red[NW][MT][NC][64];
-    const int rtile = blockIdx.x;
-    const int cgroup = blockIdx.y;
+    using C = RouterCfg<MT, NW, NC, DEPTH>;
+    extern __shared__ __align__(16) unsigned char lds[];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int twoE = 2 * E;
-    const int kq = (lane >> 4) * 8;
-    const int dq = d / NW;
-    const int kb = wave * dq + kq;
-    const bf16_t *brow[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        const int n = (cgroup * NC + c) * 16 + (lane & 15);
-        const int nc = n < twoE ? n : twoE - 1;
-        brow[c] = (nc < E ? Wg + (size_t)nc * d : Wm + (size_t)(nc - E) * d) + kb;
-    }
-    const int tbase = rtile * 16 * MT;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ncg = (E + 16 * NC - 1) / (16 * NC);  // column groups per router
+    const bool mask_half = (int)blockIdx.y >= ncg;
+    const int c0 = ((int)blockIdx.y - (mask_half ? ncg : 0)) * 16 * NC;  // first weight row
+    const int tbase = blockIdx.x * 16 * MT;
+    const int xrows = min(16 * MT, T - tbase);
+    const int wrows = min(16 * NC, E - c0);
+    const rsrc_t rx = make_rsrc(x + (size_t)tbase * d, (uint32_t)((size_t)xrows * d * 2));
+    const rsrc_t rw = make_rsrc((mask_half ? Wm : Wg) + (size_t)c0 * d,
+                                (uint32_t)((size_t)wrows * d * 2));
 
-    const bf16_t *arow[MT];
+    // load i of a chunk fills buffer rows 8i .. 8i + 7 (all x rows or all
+    // weight rows: 16 MT is a multiple of 8); lane l writes slot l % 8 of row
+    // 8i + l / 8, so it fetches piece (l % 8) ^ f(row) of that row
+    uint32_t off[C::LOADS];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        int t = tbase + m * 16 + (lane & 15);
-        t = t < T ? t : T - 1;
-        arow[m] = x + (size_t)t * d + kb;
+    for (int i = 0; i < C::LOADS; ++i) {
+        const int r = 8 * i + (lane >> 3);
+        const int piece = (lane & 7) ^ swz_f(r);
+        const int row = r < 16 * MT ? min(r, xrows - 1) : min(r - 16 * MT, wrows - 1);
+        off[i] = (uint32_t)row * (uint32_t)d * 2u + (uint32_t)piece * 16u;
     }
+    // this wave's run of chunks: [kbeg, kbeg + nk)
+    const int nkc = d >> 6;
+    const int q = nkc / NW, rm = nkc % NW;
+    const int kbeg = wave * q + min(wave, rm);
+    const int nk = q + (wave < rm ? 1 : 0);
+    unsigned char *ring = lds + wave * C::WREG;
+
+    auto issue = [&](int j) {  // chunk j of the run into buffer j % DEPTH
+        unsigned char *buf = ring + (j % DEPTH) * C::BUF;
+        const uint32_t soff = (uint32_t)(kbeg + j) * G_ROWB;
+#pragma unroll
+        for (int i = 0; i < C::LOADS; ++i)
+            lds_dma16_buf<0>(8 * i < 16 * MT ? rx : rw, off[i], soff, buf + i * 1024);
+    };
+
     f32x4 acc[MT][NC];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int c = 0; c < NC; ++c) acc[m][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    constexpr int CH = NC == 1 ? 8 : 4;  // k-steps requested per batch
-    for (int k0 = 0; k0 < dq; k0 += 32 * CH) {
-        u32x4 b[CH][NC], a[CH][MT];
-        __builtin_amdgcn_sched_barrier(0);
+    const int npro = min(DEPTH, nk);
+    for (int j = 0; j < npro; ++j) issue(j);
+    const int fr = lane & 15;
+    for (int j = 0; j < nk; ++j) {
+        router_wait_chunks<DEPTH - 1, C::LOADS>(min(DEPTH - 1, nk - 1 - j));
+        const unsigned char *buf = ring + (j % DEPTH) * C::BUF;
 #pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            const int k = k0 + 32 * j;
-            if (k < dq) {
+        for (int st = 0; st < 2; ++st) {  // two 32-wide k-steps per chunk
+            const int pc = 4 * st + (lane >> 4);
+            u32x4 a[MT], b[NC];
 #pragma unroll
-                for (int c = 0; c < NC; ++c) b[j][c] = ld16(brow[c] + k);
+            for (int m = 0; m < MT; ++m)
+                a[m] = *reinterpret_cast<const u32x4 *>(buf + swz(16 * m + fr, pc));
 #pragma unroll
-                for (int m = 0; m < MT; ++m) a[j][m] = ld16(arow[m] + k);
-            }
+            for (int c = 0; c < NC; ++c)
+                b[c] = *reinterpret_cast<const u32x4 *>(buf + swz(16 * (MT + c) + fr, pc));
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int c = 0; c < NC; ++c) acc[m][c] = mfma16x16x32(a[m], b[c], acc[m][c]);
         }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int j = 0; j < CH; ++j)
-            if (k0 + 32 * j < dq)
-#pragma unroll
-                for (int m = 0; m < MT; ++m)
-#pragma unroll
-                    for (int c = 0; c < NC; ++c) acc[m][c] = mfma16x16x32(a[j][m], b[j][c], acc[m][c]);
+        // the reads above fed the MFMAs, so the buffer is free again
+        if (j + DEPTH < nk) issue(j + DEPTH);
     }
 
+    // partial sums into this wave's own ring (all of its loads have landed),
+    // or, when they do not fit there, into slot `wave` of a layout of their
+    // own once every wave is done with its ring
+    if constexpr (!C::OWN) __syncthreads();
+    f32x4 *part = reinterpret_cast<f32x4 *>(lds + wave * C::PSTRIDE);
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int c = 0; c < NC; ++c) red[wave][m][c][lane] = acc[m][c];
+        for (int c = 0; c < NC; ++c) part[(m * NC + c) * 64 + lane] = acc[m][c];
     __syncthreads();
-    if (wave >= NC) return;
-    const int c = wave;  // this wave's column block
-    const int n = (cgroup * NC + c) * 16 + (lane & 15);
-    if (n >= twoE) return;
-    float *out = n < E ? gate_logits + n : mask_logits + (n - E);
+    for (int c = wave; c < NC; c += NW) {  // wave w sums column blocks w, w + NW, ...
+        const int n = c0 + c * 16 + fr;
+        if (n >= E) continue;
+        float *out = (mask_half ? mask_logits : gate_logits) + n;
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        f32x4 v = red[0][m][c][lane];
+        for (int m = 0; m < MT; ++m) {
+            const int slot = (m * NC + c) * 64 + lane;
+            f32x4 v = reinterpret_cast<const f32x4 *>(lds)[slot];
 #pragma unroll
-        for (int w = 1; w < NW; ++w) v += red[w][m][c][lane];
+            for (int w = 1; w < NW; ++w)
+                v += reinterpret_cast<const f32x4 *>(lds + w * C::PSTRIDE)[slot];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = tbase + m * 16 + (lane >> 4) * 4 + i;
-            if (t < T) out[(size_t)t * E] = v[i];
+            for (int i = 0; i < 4; ++i) {
+                const int t = tbase + m * 16 + (lane >> 4) * 4 + i;
+                if (t < T) out[(size_t)t * E] = v[i];
+            }
         }
     }
 }
@@ -626,8 +689,8 @@ static void launch_select(const Plan &p, const Routing &r, const Work &w, hipStr
 #ifndef BEAM_ROUTER_NARROW_T
 #define BEAM_ROUTER_NARROW_T 256
 #endif
-#ifndef BEAM_ROUTER_GEMM_T
-#define BEAM_ROUTER_GEMM_T 8192
+#ifndef BEAM_ROUTER_PAIR_T
+#define BEAM_ROUTER_PAIR_T 4096
 #endif
 #ifndef BEAM_ROUTER_BIG_T
 #define BEAM_ROUTER_BIG_T 2048
@@ -636,13 +699,28 @@ static void launch_select(const Plan &p, const Routing &r, const Work &w, hipStr
 #define BEAM_ROUTER_WIDE_T 1024
 #endif
 
+template <int MT, int NW, int NC, int DEPTH>
+static hipError_t launch_router_t(const Plan &p, const void *x, const void *Wg, const void *Wm,
+                                  const Routing &r, hipStream_t s) {
+    using C = RouterCfg<MT, NW, NC, DEPTH>;
+    static std::once_flag once;
+    static hipError_t attr_err = hipSuccess;
+    std::call_once(once, [] {
+        attr_err = hipFuncSetAttribute((const void *)router_logits_bf16<MT, NW, NC, DEPTH>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    });
+    if (attr_err != hipSuccess) return attr_err;
+    // token tiles x (column groups of W_gate, then of W_mask)
+    const dim3 grid((p.T + 16 * MT - 1) / (16 * MT), 2 * ((p.E + 16 * NC - 1) / (16 * NC)));
+    router_logits_bf16<MT, NW, NC, DEPTH><<<grid, NW * 64, C::LDS, s>>>(
+        (const bf16_t *)x, (const bf16_t *)Wg, (const bf16_t *)Wm, r.gate_logits, r.mask_logits,
+        p.T, p.d, p.E);
+    return hipGetLastError();
+}
+
 hipError_t launch_router_logits(const Plan &p, const void *x, const void *Wg, const void *Wm,
                                 const Routing &r, hipStream_t s) {
-    if (p.dtype == 1 && p.path == 1 && p.T > BEAM_ROUTER_GEMM_T) {
-        // large batch: the logits as one dense MFMA GEMM
-        hipError_t err = launch_gemm_router(p, x, Wg, Wm, r, s);
-        if (err != hipSuccess) return err;
-    } else if (p.small) {
+    if (p.small) {
         router_logits_small<<<(2 * p.E + 3) / 4, 256, 0, s>>>(
             (const bf16_t *)x, (const bf16_t *)Wg, (const bf16_t *)Wm, r.gate_logits,
             r.mask_logits, p.T, p.d, p.E);
@@ -651,30 +729,19 @@ hipError_t launch_router_logits(const Plan &p, const void *x, const void *Wg, co
         // most workgroups, the fewest bytes per workgroup); more: 32-token
         // tiles; large batches: tiles of four column blocks, so x and the
         // weights are each re-read fewer times (32 tokens up to 2048, then 64
-        // tokens with four waves per workgroup, two workgroups per CU)
-        const int mt = p.T <= BEAM_ROUTER_NARROW_T ? 1
-                       : p.T <= BEAM_ROUTER_WIDE_T ? 2 : p.T <= BEAM_ROUTER_BIG_T ? 2 : 4;
-        const int ncb = p.T <= BEAM_ROUTER_WIDE_T ? 1 : 4;
-        const dim3 grid((p.T + 16 * mt - 1) / (16 * mt), (2 * p.E + 16 * ncb - 1) / (16 * ncb));
-#define BEAM_ROUTER(MTV, NWV, NCV)                                                             \
-    router_logits_bf16<MTV, NWV, NCV><<<grid, NWV * 64, 0, s>>>(                              \
-        (const bf16_t *)x, (const bf16_t *)Wg, (const bf16_t *)Wm, r.gate_logits,            \
-        r.mask_logits, p.T, p.d, p.E)
-        // eight waves split d in 256-wide parts (d % 256 == 0), four in d / 4
-        const bool d256 = p.d % 256 == 0;
-        if (mt == 1) {
-            if (d256) BEAM_ROUTER(1, 8, 1);
-            else BEAM_ROUTER(1, 4, 1);
-        } else if (ncb == 1) {
-            if (d256) BEAM_ROUTER(2, 8, 1);
-            else BEAM_ROUTER(2, 4, 1);
-        } else if (mt == 2) {
-            if (d256) BEAM_ROUTER(2, 8, 4);
-            else BEAM_ROUTER(2, 4, 4);
-        } else {
-            BEAM_ROUTER(4, 4, 4);
-        }
-#undef BEAM_ROUTER
+        // tokens with four waves per workgroup).  Up to 4096 tokens the rings
+        // fill 96-128 KB of LDS (one workgroup per CU, each wave two chunks
+        // deep where that fits); above, single-chunk rings of 64 KB let two
+        // workgroups share a CU (at 8192 tokens 36.6 against 39.8 us for the
+        // whole routing call; with fewer than two workgroups per CU the pairs
+        // leave CUs idle instead)
+        hipError_t err;
+        if (p.T <= BEAM_ROUTER_NARROW_T) err = launch_router_t<1, 8, 1, 4>(p, x, Wg, Wm, r, s);
+        else if (p.T <= BEAM_ROUTER_WIDE_T) err = launch_router_t<2, 8, 1, 2>(p, x, Wg, Wm, r, s);
+        else if (p.T <= BEAM_ROUTER_BIG_T) err = launch_router_t<2, 8, 4, 1>(p, x, Wg, Wm, r, s);
+        else if (p.T <= BEAM_ROUTER_PAIR_T) err = launch_router_t<4, 4, 4, 2>(p, x, Wg, Wm, r, s);
+        else err = launch_router_t<4, 4, 4, 1>(p, x, Wg, Wm, r, s);
+        if (err != hipSuccess) return err;
     } else {
         const long long n = (long long)p.T * 2 * p.E;
         router_logits_generic<float><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(

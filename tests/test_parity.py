@@ -264,10 +264,11 @@ def test_router_tiles_large_batch(T):
     _full_check(L, 2)
 
 
-# above 8192 tokens the logits come from the router GEMM (128-token tiles):
-# last tiles holding 1 and 108 tokens (every logit and route is checked)
-@pytest.mark.parametrize("T", [8193, 8300])
-def test_router_gemm_ragged(T):
+# above 4096 tokens the router's 64-token tiles take single-chunk LDS rings
+# (two workgroups per CU): last tiles holding 1 and 44 tokens (every logit
+# and route is checked); d = 128 gives two 64-wide k-chunks for four waves
+@pytest.mark.parametrize("T", [4097, 8300])
+def test_router_pair_tiles_ragged(T):
     L = layer(SMALL, T, seed=1250 + T, mask_bias=0.0)
     _full_check(L, 2)
 

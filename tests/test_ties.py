@@ -1,6 +1,6 @@
 """GPU: the Top-K tie rule and the mask at z = 0 exactly, through both select
 kernels (one workgroup for a batch of at most 64 tokens; quarter-tile
-workgroups above) and the router GEMM of large batches.
+workgroups above) and the router-logit tilings of small and large batches.
 
 BEAM paper, section 3.2 Eq. 4 keeps the K largest router logits; equal logits
 go to the lower expert index first (the slot order is descending logit, then
@@ -29,7 +29,7 @@ from beamtest import (check_logits, check_routing_exact, check_y, gpu_routing_ho
 pytestmark = pytest.mark.gpu
 
 # E = 128: 8 experts per select lane (16 lanes per token); d % 256 == 0 and
-# I % 128 == 0, so batches above 8192 tokens take the router GEMM
+# I % 128 == 0: batches above 512 tokens take the tiled path
 def _shape(K):
     return synth.LayerShape(256, 128, K, 128, torch.bfloat16)
 
