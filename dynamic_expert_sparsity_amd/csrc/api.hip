@@ -376,6 +376,9 @@ int beam_moe_mask_backward(const beam_moe_desc *desc, const void *x, const void 
         return fail(BEAM_EINVAL, "d_gate_logits is not 4-byte aligned");
     if (!std::isfinite(beta)) return fail(BEAM_EINVAL, "beta is not finite");
     const BwdPlan b = mask_backward_plan(p);
+    // the dW contraction addresses dz transposed with 32-bit byte offsets
+    if (p.dtype == 1 && dW_mask && (unsigned long long)b.E_pad * b.T_pad * 2 >= (1ull << 32))
+        return fail(BEAM_EUNSUPPORTED, "dW_mask of a bf16 layer needs E * T * 2 < 2^32 (T=%d)", p.T);
     if (b.bytes > 0 && !aligned(ws, 16))
         return fail(BEAM_EINVAL, "workspace is NULL or not 16-byte aligned");
     if (ws_bytes < b.bytes)

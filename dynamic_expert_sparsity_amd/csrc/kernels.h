@@ -94,10 +94,11 @@ hipError_t launch_down_small(const Plan &p, const void *W_dt, const Routing &r, 
                              void *y, hipStream_t s);
 // mask-router backward: workspace layout and launches
 struct BwdPlan {
-    int T_pad, E_pad;       // tokens rounded up to the dW chunk, experts to 16
+    int T_pad, E_pad;       // tokens rounded up to the dW stage, experts to 16
     int n_split;            // token ranges of the dW contraction
-    int t_per_split;        // tokens per range (a multiple of the chunk)
-    size_t off_dzT, off_part, bytes;
+    int t_per_split;        // tokens per range (a multiple of the stage)
+    int dx_tok;             // tokens per dx workgroup (a multiple of 16)
+    size_t off_dzT, off_dzk, off_part, bytes;  // workspace carve-up (bf16 layers)
 };
 BwdPlan mask_backward_plan(const Plan &p);
 hipError_t launch_mask_backward(const Plan &p, const BwdPlan &b, const void *x, const void *Wm,

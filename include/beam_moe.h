@@ -221,7 +221,9 @@ int beam_moe_forward_noalloc(const beam_moe_desc *desc, const void *x, const voi
  * on the matrix cores from d_mask_logits rounded to bf16 (float32
  * accumulation); dx and the other outputs use float32 arithmetic.
  * ws: at least sizes.mask_backward_workspace_bytes (may be 0 for float32
- * layers).  Errors as for beam_moe_forward; beta must be finite. */
+ * layers).  Errors as for beam_moe_forward; beta must be finite;
+ * BEAM_EUNSUPPORTED for dW_mask of a bf16 layer with E * T * 2 >= 2^32
+ * (E and T rounded up to 16 and 64). */
 int beam_moe_mask_backward(const beam_moe_desc *desc, const void *x, const void *W_mask,
                            const beam_moe_routing *routing, const float *slot_grad, float beta,
                            float *d_mask_logits, float *dW_mask, float *dx,

@@ -81,3 +81,26 @@ def test_mask_backward_optional_outputs():
     torch.cuda.synchronize()
     for k in ("dz", "dW_mask", "dx", "d_gate"):
         assert torch.equal(again[k], full[k]), k
+
+
+@pytest.mark.parametrize("T", [96, 3000])
+def test_mask_backward_each_output_alone(T):
+    """dW alone (its token-range partials added by a reduction of their own
+    at T = 3000) and dx alone (no partials to add) equal, bit for bit, what
+    a call asking for every output writes."""
+    need_gpu()
+    sh = synth.SHAPES["qwen3"]
+    L = synth.make_layer("qwen3", T, seed=3300 + T, mask_bias=-0.5, device="cuda")
+    lay = B.MoELayer(L["W_gate"], L["W_mask"], L["W_gu"], L["W_dt"], sh.K)
+    lay(L["x"])
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(T)
+    sg = torch.randn((T, sh.K), generator=gen, device="cuda", dtype=torch.float32)
+    full = lay.mask_backward(L["x"], sg, 0.01)
+    only_dw = lay.mask_backward(L["x"], sg, 0.01, want_dx=False, want_d_gate=False)
+    only_dx = lay.mask_backward(L["x"], sg, 0.01, want_dW=False, want_d_gate=False)
+    torch.cuda.synchronize()
+    assert only_dw["dx"] is None and only_dx["dW_mask"] is None
+    assert torch.equal(only_dw["dW_mask"], full["dW_mask"])
+    assert torch.equal(only_dx["dx"], full["dx"])
+    assert torch.equal(only_dw["dz"], full["dz"]) and torch.equal(only_dx["dz"], full["dz"])
