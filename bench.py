@@ -91,6 +91,9 @@ def parse():
     ap.add_argument("--backward", action="store_true", default=True,
                     help="also time the mask-router backward at T = 256, 2048, 8192")
     ap.add_argument("--no-backward", dest="backward", action="store_false")
+    ap.add_argument("--only-backward", action="store_true",
+                    help="time the mask-router backward only (no decode headline, sweep, prefill "
+                         "or CPU baseline)")
     ap.add_argument("--shared", action="store_true", default=True,
                     help="also measure the DeepSeekV2-Lite-shaped layer with 2 shared experts")
     ap.add_argument("--no-shared", dest="shared", action="store_false")
@@ -111,8 +114,9 @@ COUNTERS = os.path.join(HERE, "profiles", "decode_d2048_E128_K8_I768_T256_hbm_co
 def counted_traffic():
     """Calibrated HBM bytes per launch of the dominant decode kernel, from the
     committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary of the headline
-    workload; None when that summary is missing or the kernel source has
-    changed since the counters were taken."""
+    workload; None when that summary is missing or any of the kernel's
+    source files (a comma list, hashed in order) has changed since the
+    counters were taken."""
     import hashlib
     try:
         kv = {}
@@ -121,8 +125,10 @@ def counted_traffic():
             if line.startswith("traffic_") and ":" in line:
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-        src = os.path.join(HERE, kv["traffic_source"])
-        if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv["traffic_source_sha256"]:
+        h = hashlib.sha256()
+        for name in kv["traffic_source"].split(","):
+            h.update(open(os.path.join(HERE, name.strip()), "rb").read())
+        if h.hexdigest() != kv["traffic_source_sha256"]:
             return None
         return {"kernel": kv["traffic_kernel"], "bytes": int(kv["traffic_bytes_per_launch"])}
     except (OSError, KeyError, ValueError):
@@ -389,6 +395,12 @@ def main():
                 f"MFMA {r['mfma_frac_layer']:.3f}, roofline {r['roofline_frac']:.3f}")
         return prefill_out
 
+    if args.only_backward:
+        print(json.dumps({"metric": METRIC, "unit": "tok/s", "n_gpus": 1, "dtype": "bf16",
+                          "data": "synthetic",
+                          "mask_backward": run_backward(B, sets, shape, dev)}), flush=True)
+        return
+
     if args.only_prefill:
         prefill_out = run_prefill()
         print(json.dumps({"metric": METRIC, "unit": "tok/s", "n_gpus": 1, "dtype": "bf16",
@@ -600,11 +612,15 @@ def run_stack(B, synth, sets, shape, dev, T, steps, dims):
     return out
 
 
-def run_backward(B, sets, shape, dev, steps=20):
+def run_backward(B, sets, shape, dev, steps=20, batch=10):
     """beam_moe_mask_backward after a forward of the headline layer, T = 256,
-    2048 and 8192 tokens (slot gradients drawn once per T).  Algorithmic
-    bytes: x read (T d bf16), dx and the two [T, E] float32 logit gradients
-    written, dW_mask written; FLOPs of the dW contraction 2 T E d."""
+    2048 and 8192 tokens (slot gradients drawn once per T).  Each sample
+    times `batch` calls enqueued back to back between two events and counts
+    their mean: the device time of a call, without the binding's per-call
+    host work (four output allocations and the ctypes call, some 15 us,
+    which the device otherwise spends idle).  Algorithmic bytes: x read
+    (T d bf16), dx and the two [T, E] float32 logit gradients written,
+    dW_mask written; FLOPs of the dW contraction 2 T E d."""
     import torch
 
     d, E, K = shape.d, shape.E, shape.K
@@ -627,10 +643,11 @@ def run_backward(B, sets, shape, dev, steps=20):
                for _ in range(steps)]
         for a, b in evs:
             a.record()
-            lay.mask_backward(x, sg, 0.01)
+            for _ in range(batch):
+                lay.mask_backward(x, sg, 0.01)
             b.record()
         torch.cuda.synchronize()
-        per = [a.elapsed_time(b) for a, b in evs]
+        per = [a.elapsed_time(b) / batch for a, b in evs]
         ms = pct(per, 0.5)
         byts = T * d * 2 + T * d * 4 + 2 * T * E * 4 + E * d * 4
         flops = 2.0 * T * E * d
@@ -640,7 +657,8 @@ def run_backward(B, sets, shape, dev, steps=20):
                     "dW_TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2)})
         log(f"mask backward T={T}: {ms * 1e3:.1f} us")
         del lay
-    return {"workload": f"d{d}-E{E}-K{K}-bf16 mask router backward, beta 0.01", "runs": out}
+    return {"workload": f"d{d}-E{E}-K{K}-bf16 mask router backward, beta 0.01",
+            "timing": f"mean of {batch} calls enqueued back to back per sample", "runs": out}
 
 
 def run_shared(B, synth, dev, measure, args):
