@@ -80,7 +80,8 @@ extern "C" {
 
 /* stage ids for the optional per-stage events of beam_moe_forward_ex */
 #define BEAM_STAGE_ROUTER   0 /* a1-a4: router logits, top-K, softmax, mask,
-                                 g_hat, -1 ids, counts, offsets, lists            */
+                                 g_hat, -1 ids, counts, offsets, lists (batches
+                                 of at most 8 tokens: the logits only)            */
 #define BEAM_STAGE_SELECT   1 /* (inside BEAM_STAGE_ROUTER: empty)                */
 #define BEAM_STAGE_SCAN     2 /* (inside BEAM_STAGE_ROUTER: empty)                */
 #define BEAM_STAGE_SCATTER  3 /* a4: pairs into per-expert lists, T > 1024 only   */
@@ -172,8 +173,12 @@ int beam_moe_forward(const beam_moe_desc *desc, const void *x, const void *W_gat
  * caller-created event or NULL (not recorded); event i is recorded on
  * `stream` just before stage i is enqueued and event BEAM_NUM_STAGES after
  * the last stage (a stage that the chosen path fuses into another one, or
- * skips, has equal start and end events).  Each record is a separate stream
- * command and adds a few microseconds between the stages it separates. */
+ * skips, has equal start and end events).  Decode batches of at most 8
+ * tokens (bf16, streaming path, K + n_shared <= 32, T d * 2 and
+ * (K + n_shared) I * 2 bytes at most 48 KB each) run three launches: stage ROUTER holds the router
+ * logits only, the rest of a1-a4 runs inside stage UP and the combine inside
+ * stage DOWN.  Each record is a separate stream command and adds a few
+ * microseconds between the stages it separates. */
 int beam_moe_forward_ex(const beam_moe_desc *desc, const void *x, const void *W_gate,
                         const void *W_mask, const void *W_gu, const void *W_dt,
                         void *y, const beam_moe_routing *out, void *ws,
