@@ -146,6 +146,7 @@ int make_plan(const beam_moe_desc *desc, Plan &p) {
     size_t off = 0;
     p.off_tile_mask = off; off = align_up(off + (size_t)p.n_tiles * p.E2 * 8, 256);
     p.off_tile_base = off; off = align_up(off + (size_t)p.n_tiles * p.E2 * 4, 256);
+    p.off_cnt = off;       off = align_up(off + (size_t)p.E2 * 4, 256);
     p.off_pair_pos = off;  off = align_up(off + (size_t)PT * 4, 256);
     p.off_meta = off;      off = align_up(off + 16, 256);
     // position blocks of <= 32: at most one partial block per active expert
@@ -184,6 +185,7 @@ Work carve(const Plan &p, void *ws) {
     Work w;
     w.tile_mask = reinterpret_cast<uint64_t *>(b + p.off_tile_mask);
     w.tile_base = reinterpret_cast<int32_t *>(b + p.off_tile_base);
+    w.cnt = reinterpret_cast<int32_t *>(b + p.off_cnt);
     w.pair_pos = reinterpret_cast<int32_t *>(b + p.off_pair_pos);
     w.meta = reinterpret_cast<int32_t *>(b + p.off_meta);
     w.pbt = reinterpret_cast<int32_t *>(b + p.off_pbt);

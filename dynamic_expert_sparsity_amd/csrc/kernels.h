@@ -37,7 +37,8 @@ struct Plan {
     long long n_blocks_cap; // block_expert capacity
     int max_active;     // host upper bound on experts with >= 1 active pair
     // workspace carve-up (byte offsets) and totals
-    size_t off_tile_mask, off_tile_base, off_pair_pos, off_meta, off_pbt, off_stok, off_h, off_o;
+    size_t off_tile_mask, off_tile_base, off_cnt, off_pair_pos, off_meta, off_pbt, off_stok, off_h,
+        off_o;
     size_t route_bytes, total_bytes;
 };
 
@@ -55,6 +56,7 @@ struct Routing {
 struct Work {  // workspace views
     uint64_t *tile_mask;
     int32_t *tile_base;
+    int32_t *cnt;        // [E + S] per-expert active-pair counts (batches of > 16 tiles)
     int32_t *pair_pos;   // [T*K] sorted position of each pair, -1 if masked
     int32_t *meta;       // [4] the call's record {mode (1 tiled, 0 streaming),
                          // max count, position blocks, 0}
@@ -72,7 +74,10 @@ hipError_t launch_router_logits(const Plan &p, const void *x, const void *Wg, co
                                 const Routing &r, hipStream_t s);
 hipError_t launch_route(const Plan &p, const void *x, const void *Wg, const void *Wm,
                         const Routing &r, const Work &w, hipStream_t s);
-// pair scatter for large batches (no-op when the routing kernel placed them)
+// batches of more than 16 tiles: per-expert tile bases and counts (after the
+// select), then offsets and the pair scatter (a no-op for smaller batches,
+// whose routing kernel placed the pairs)
+hipError_t launch_bases(const Plan &p, const Work &w, hipStream_t s);
 hipError_t launch_scatter(const Plan &p, const Routing &r, const Work &w, hipStream_t s);
 // the tiled path (bf16): one launch per projection runs the kernel family
 // the compaction picked for the call (streaming, 128-row or 256-row tiles)

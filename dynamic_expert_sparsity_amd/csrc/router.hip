@@ -418,29 +418,23 @@ __global__ __launch_bounds__(256) void select_topk_mask(int T, int E, int S, int
         dst[4 * e] = (uint16_t)(e < E ? tmask[e] : tile_all(tile, T) >> (16 * q));
 }
 
-// The grouping of a batch of tiles by one workgroup (and the pair positions
-// when the batch is small).  KEEPW (batches of more than 16 tiles): keep each
-// thread's tile words in registers between the two passes; the pairs are
-// placed by a separate kernel.  Else (at most 16 tiles, fuse_scatter set):
-// the tile words and bases stay in LDS and the pairs are placed here.
-template <bool KEEPW>
+// The grouping of a batch of at most 16 tiles by one workgroup, the pairs
+// placed here too (larger batches: compact_bases after the select,
+// compact_scatter as the next stage).
 __global__ __launch_bounds__(1024) void compact_tiles(const uint64_t *__restrict__ tile_mask,
                                                       int n_tiles, int E, int S, int bm, int K,
                                                       int TK, Routing r,
-                                                      int32_t *__restrict__ tile_base,
                                                       int32_t *__restrict__ pair_pos,
                                                       int32_t *__restrict__ meta,
                                                       int32_t *__restrict__ sorted_tok,
-                                                      int32_t *__restrict__ pbt,
-                                                      int fuse_scatter, int split) {
+                                                      int32_t *__restrict__ pbt, int split) {
     __shared__ int s_part[1024];
     __shared__ int s_cnt[256];
     __shared__ int s_off[257];
-    __shared__ uint64_t s_words[KEEPW ? 1 : 16 * 256];
-    __shared__ int32_t s_tb[KEEPW ? 1 : 16 * 256];
-    scan_tiles<KEEPW, !KEEPW>(tile_mask, n_tiles, E, S, bm, K, TK, r, tile_base, pair_pos, meta,
-                              sorted_tok, pbt, fuse_scatter != 0, split, threadIdx.x, 1024,
-                              s_part, s_cnt, s_off, s_words, s_tb);
+    __shared__ uint64_t s_words[16 * 256];
+    __shared__ int32_t s_tb[16 * 256];
+    scan_tiles(tile_mask, n_tiles, E, S, bm, K, TK, r, pair_pos, meta, sorted_tok, pbt, split,
+               threadIdx.x, 1024, s_part, s_cnt, s_off, s_words, s_tb);
 }
 
 // The routing of a small batch (T <= 64, one tile) by one workgroup of
@@ -665,14 +659,12 @@ static void launch_select_t(const Plan &p, const Routing &r, const Work &w, hipS
     } else {
         select_topk_mask<EJ><<<p.n_tiles * 4, 256, 0, s>>>(p.T, p.E, p.S, p.K, p.thr, r,
                                                           w.tile_mask);
-        if (!p.fuse_scatter)  // more than 16 tiles
-            compact_tiles<true><<<1, 1024, 0, s>>>(w.tile_mask, p.n_tiles, p.E, p.S, p.bm, p.K,
-                                                   p.T * p.K, r, w.tile_base, w.pair_pos, w.meta,
-                                                   w.sorted_tok, w.pbt, p.fuse_scatter, p.split);
+        if (!p.fuse_scatter)  // more than 16 tiles: bases here, offsets with the scatter
+            launch_bases(p, w, s);
         else
-            compact_tiles<false><<<1, 1024, 0, s>>>(w.tile_mask, p.n_tiles, p.E, p.S, p.bm, p.K,
-                                                    p.T * p.K, r, w.tile_base, w.pair_pos, w.meta,
-                                                    w.sorted_tok, w.pbt, p.fuse_scatter, p.split);
+            compact_tiles<<<1, 1024, 0, s>>>(w.tile_mask, p.n_tiles, p.E, p.S, p.bm, p.K,
+                                             p.T * p.K, r, w.pair_pos, w.meta, w.sorted_tok,
+                                             w.pbt, p.split);
     }
 }
 

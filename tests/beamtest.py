@@ -167,12 +167,12 @@ def keep_rate_bound(p, n):
 
 def mode_record(lay):
     """The call's kernel-family record {family, max count, records, layout} from
-    the workspace (layout: tile token sets, tile bases, pair positions, then
-    the record, each piece rounded up to 256 bytes)."""
+    the workspace (layout: tile token sets, tile bases, per-expert counts,
+    pair positions, then the record, each piece rounded up to 256 bytes)."""
     al = lambda v: (v + 255) // 256 * 256  # noqa: E731
     T, E2, K, S = lay.desc.T, lay.desc.E + lay.desc.n_shared, lay.desc.K, lay.desc.n_shared
     n_tiles = (T + 63) // 64
-    off = al(n_tiles * E2 * 8) + al(n_tiles * E2 * 4) + al(T * (K + S) * 4)
+    off = al(n_tiles * E2 * 8) + al(n_tiles * E2 * 4) + al(E2 * 4) + al(T * (K + S) * 4)
     return lay.ws[off:off + 16].view(torch.int32).cpu().numpy()
 
 
