@@ -259,10 +259,6 @@ __global__ __launch_bounds__(256) void router_logits_generic(
 // values that are the same pair for both partners, so every lane of the
 // group ends with the same result (also for the float sum).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ bool beats(float v, int e, float bv, int be) {
-    return v > bv || (v == bv && e < be);
-}
-
 constexpr int DPP_QUAD_1032 = 0xB1;  // quad_perm [1,0,3,2]
 constexpr int DPP_QUAD_2301 = 0x4E;  // quad_perm [2,3,0,1]
 constexpr int DPP_ROW_HALF_MIRROR = 0x141;
@@ -277,23 +273,41 @@ __device__ __forceinline__ float dpp_f(float v) {
     return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
 }
 
-constexpr int NO_EXPERT = 0x7fffffff;
+// Selection keys: 64-bit words that order like (value desc, expert asc).
+// High word: the logit's bits mapped to an unsigned order (negative values
+// inverted, positive ones with the sign bit set; -0 folded into +0 first, so
+// the two zeros tie as they compare equal); low word: ~expert.  The Top-K
+// rounds then take plain maxima of keys, which compile to compares and
+// selects (a value-and-index form with branches took ~0.5 us per round in
+// the single-wave select of a small batch).
+__device__ __forceinline__ unsigned long long sel_key(float v, int e) {
+    const unsigned b = __float_as_uint(v + 0.f);
+    const unsigned o = b ^ ((unsigned)((int)b >> 31) | 0x80000000u);
+    return ((unsigned long long)o << 32) | (unsigned)~e;
+}
+__device__ __forceinline__ float key_value(unsigned long long key) {
+    const unsigned o = (unsigned)(key >> 32);
+    return __uint_as_float(o ^ (((o >> 31) - 1u) | 0x80000000u));
+}
+__device__ __forceinline__ int key_expert(unsigned long long key) { return (int)~(unsigned)key; }
 
 template <int CTRL>
-__device__ __forceinline__ void argmax_step(float &bv, int &be) {
-    const float ov = dpp_f<CTRL>(bv);
-    const int oe = dpp_i<CTRL>(be);
-    if (oe != NO_EXPERT && (be == NO_EXPERT || beats(ov, oe, bv, be))) {
-        bv = ov;
-        be = oe;
-    }
+__device__ __forceinline__ unsigned long long dpp_key(unsigned long long v) {
+    const unsigned lo = (unsigned)dpp_i<CTRL>((int)(unsigned)v);
+    const unsigned hi = (unsigned)dpp_i<CTRL>((int)(unsigned)(v >> 32));
+    return ((unsigned long long)hi << 32) | lo;
 }
-
-__device__ __forceinline__ void row_argmax(float &bv, int &be) {
-    argmax_step<DPP_QUAD_1032>(bv, be);
-    argmax_step<DPP_QUAD_2301>(bv, be);
-    argmax_step<DPP_ROW_HALF_MIRROR>(bv, be);
-    argmax_step<DPP_ROW_MIRROR>(bv, be);
+template <int CTRL>
+__device__ __forceinline__ unsigned long long key_max_step(unsigned long long v) {
+    const unsigned long long o = dpp_key<CTRL>(v);
+    return o > v ? o : v;
+}
+// largest key of a row of 16 lanes, in every lane of the row
+__device__ __forceinline__ unsigned long long row_max_key(unsigned long long v) {
+    v = key_max_step<DPP_QUAD_1032>(v);
+    v = key_max_step<DPP_QUAD_2301>(v);
+    v = key_max_step<DPP_ROW_HALF_MIRROR>(v);
+    return key_max_step<DPP_ROW_MIRROR>(v);
 }
 
 __device__ __forceinline__ float row_sum(float v) {
@@ -312,7 +326,8 @@ __device__ __forceinline__ void select_group(
     int lane, bool write = true) {
     using MW = std::conditional_t<TB == 64, unsigned long long, unsigned>;
     static_assert(TB == 64 || TB == 16, "token bits per mask word");
-    static_assert(EJ >= 1 && EJ <= 16, "at most 16 experts per lane (E <= 256)");
+    static_assert(EJ >= 1 && EJ <= 16 && (EJ & (EJ - 1)) == 0,
+                  "a power of two, at most 16 experts per lane (E <= 256)");
     const int i = lane & 15;
     const int t = t_first + (lane >> 4);
     const bool valid = t < T;
@@ -337,33 +352,44 @@ __device__ __forceinline__ void select_group(
 #pragma unroll
         for (int j = 0; j < EJ; ++j) rv[j] = e0 + j < E ? gr[j] : 0.f;
     }
-    unsigned live = 0;
+    // candidate keys (0 below every key: no expert, or already taken)
+    unsigned long long key[EJ];
 #pragma unroll
-    for (int j = 0; j < EJ; ++j)
-        if (e0 + j < E) live |= 1u << j;
+    for (int j = 0; j < EJ; ++j) key[j] = e0 + j < E ? sel_key(rv[j], e0 + j) : 0ull;
 
-    // slot k is kept by lane k
-    float v0 = 0.f, myv = 0.f;
-    int mye = 0;
-    for (int k = 0; k < K; ++k) {
-        float bv = 0.f;
-        int be = NO_EXPERT;
+    // each lane's keys in descending order (a bitonic network, EJ a power of
+    // two), so a lane's best remaining candidate is always key[0]
 #pragma unroll
-        for (int j = 0; j < EJ; ++j) {  // expert index ascends with j: ties keep the first
-            if (((live >> j) & 1u) && (be == NO_EXPERT || rv[j] > bv)) {
-                bv = rv[j];
-                be = e0 + j;
+    for (int w = 2; w <= EJ; w <<= 1)
+#pragma unroll
+        for (int h = w >> 1; h > 0; h >>= 1)
+#pragma unroll
+            for (int a = 0; a < EJ; ++a) {
+                const int c = a ^ h;
+                if (c > a) {
+                    const unsigned long long hi = key[a] > key[c] ? key[a] : key[c];
+                    const unsigned long long lo = key[a] > key[c] ? key[c] : key[a];
+                    const bool desc = (a & w) == 0;
+                    key[a] = desc ? hi : lo;
+                    key[c] = desc ? lo : hi;
+                }
             }
-        }
-        row_argmax(bv, be);
-        const int jw = be - e0;
-        if (jw >= 0 && jw < EJ) live &= ~(1u << jw);
-        if (k == 0) v0 = bv;
-        if (k == i) {
-            myv = bv;
-            mye = be;
-        }
+    // round k takes the row's largest head; the lane that held it moves its
+    // list up by one.  Slot k is kept by lane k.
+    unsigned long long top = 0ull, kept = 0ull;
+    for (int k = 0; k < K; ++k) {
+        const unsigned long long b = row_max_key(key[0]);
+        // all ones in the lane that held the head: a bit-select per word
+        // (v_bfi_b32) moves its list up
+        const unsigned long long m = 0ull - (unsigned long long)(key[0] == b);
+#pragma unroll
+        for (int j = 0; j + 1 < EJ; ++j) key[j] = (key[j + 1] & m) | (key[j] & ~m);
+        key[EJ - 1] &= ~m;
+        top = k == 0 ? b : top;
+        kept = k == i ? b : kept;
     }
+    const float v0 = key_value(top), myv = key_value(kept);
+    const int mye = key_expert(kept);
 
     const float num = i < K ? expf(myv - v0) : 0.f;
     const float den = row_sum(num);
@@ -479,6 +505,51 @@ __device__ __forceinline__ void route_small_body(
     }
 }
 
+// The part of route_small_body that the expert items of a small batch need,
+// in LDS only: the token sets tmask[e] (routed experts), the block-padded
+// list offsets s_off[e] (the same formula as offsets_from_counts, so the
+// positions equal the ones the routing outputs describe) and the ascending
+// list of active experts (routed experts with a pair, then every shared
+// expert) with its length.
+template <int EJ>
+__device__ __forceinline__ void route_small_active(int T, int E, int S, int K, float thr, int bm,
+                                                   const Routing &r, int tid,
+                                                   unsigned long long *tmask, int *s_off,
+                                                   int *s_act, int *s_nact) {
+    if (tid < E) tmask[tid] = 0ull;
+    __syncthreads();
+    if ((tid >> 6) * 4 < T)  // four tokens per wave
+        select_group<EJ, 64>(T, E, K, thr, r, tmask, nullptr, (tid >> 6) * 4, tid & 63, false);
+    __syncthreads();
+    if (tid < 64) {
+        // four experts per lane, in expert order
+        const int E2 = E + S;
+        int act[4], pad[4], sa = 0, sp = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int ex = tid * 4 + j;
+            const int c = ex < E ? __popcll(tmask[ex]) : (ex < E2 ? T : 0);
+            act[j] = c > 0 ? 1 : 0;
+            pad[j] = (c + bm - 1) / bm * bm;
+            sa += act[j];
+            sp += pad[j];
+        }
+        const int ia = wave_incl_scan(sa, tid);
+        const int ip = wave_incl_scan(sp, tid);
+        int oa = ia - sa, op = ip - sp;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int ex = tid * 4 + j;
+            if (ex < E2) s_off[ex] = op;
+            if (act[j]) s_act[oa] = ex;
+            oa += act[j];
+            op += pad[j];
+        }
+        if (tid == 63) *s_nact = ia;
+    }
+    __syncthreads();
+}
+
 // A small batch (T <= 64, one tile) in one workgroup.
 template <int EJ>
 __global__ __launch_bounds__(1024) void route_small(int T, int E, int S, int K, float thr, int bm,
@@ -530,16 +601,23 @@ __global__ __launch_bounds__(512) void up_small(int T, int E, int S, int K, floa
     const int tid = threadIdx.x;
     const int nch = d >> 3;  // 16-byte chunks per row
     // the batch's x rows: requested before the routing, stored to LDS after
-    // it (T * d * 2 <= 48 KB: at most 6 chunks per thread)
+    // it (T * d * 2 <= 48 KB: at most 6 chunks per thread).  Every load is
+    // issued (past the end: chunk 0 again), so none is waited for before the
+    // routing.
     constexpr int XR = 6;
     u32x4 xr[XR];
 #pragma unroll
     for (int k = 0; k < XR; ++k) {
         const int i = tid + 512 * k;
-        if (i < T * nch) xr[k] = ld16(x + (size_t)i * 8);
+        xr[k] = ld16(x + (size_t)(i < T * nch ? i : 0) * 8);
     }
-    route_small_body<EJ>(T, E, S, K, thr, bm, r, pair_pos, meta, sorted_tok, pbt, split,
-                         blockIdx.x == 0, tid, 512, tmask, s_mid, s_cnt, s_off, s_act, &s_nact);
+    // workgroup 0 writes every routing output; the others only need the
+    // token sets and the active-expert list
+    if (blockIdx.x == 0)
+        route_small_body<EJ>(T, E, S, K, thr, bm, r, pair_pos, meta, sorted_tok, pbt, split,
+                             true, tid, 512, tmask, s_mid, s_cnt, s_off, s_act, &s_nact);
+    else
+        route_small_active<EJ>(T, E, S, K, thr, bm, r, tid, tmask, s_off, s_act, &s_nact);
 #pragma unroll
     for (int k = 0; k < XR; ++k) {
         const int i = tid + 512 * k;
