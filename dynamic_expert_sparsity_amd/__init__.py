@@ -221,9 +221,18 @@ def _gpu_tensor(name, t, dtype=None, shape=None):
     return t
 
 
-def _stream_ptr(stream) -> int:
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return int(s.cuda_stream)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream_ptr(stream, device: int) -> int:
+    """The HIP stream handle to launch on: `stream`, else the current stream
+    of GPU `device` (read without building a Stream object, which costs a few
+    us per call)."""
+    if stream is not None:
+        return int(stream.cuda_stream)
+    if _raw_stream is not None:
+        return _raw_stream(device)
+    return int(torch.cuda.current_stream(device).cuda_stream)
 
 
 class MoELayer:
@@ -248,6 +257,7 @@ class MoELayer:
         self.d, self.E, self.K, self.I = d, E, int(K), I
         self.S = E2 - E
         self.block_m, self.flags, self.tau = block_m, flags, tau
+        self._dev = W_gate.get_device()
         self._T = None
 
     def prepare(self, T):
@@ -283,7 +293,7 @@ class MoELayer:
         _check(lib().beam_moe_forward_ex(
             ctypes.byref(self.desc), x.data_ptr(), self.W_gate.data_ptr(), self.W_mask.data_ptr(),
             self.W_gu.data_ptr(), self.W_dt.data_ptr(), self.y.data_ptr(), ctypes.byref(self._rs),
-            self.ws.data_ptr(), self.ws.numel(), _stream_ptr(stream), ev))
+            self.ws.data_ptr(), self.ws.numel(), _stream_ptr(stream, self._dev), ev))
         return self.y, self.routing
 
     __call__ = forward
@@ -311,7 +321,7 @@ class MoELayer:
         _check(lib().beam_moe_mask_backward(
             ctypes.byref(self.desc), x.data_ptr(), self.W_mask.data_ptr(), ctypes.byref(self._rs),
             slot_grad.data_ptr(), float(beta), dz.data_ptr(), ptr(dW), ptr(dx), ptr(dg),
-            self._bws.data_ptr(), self._bws.numel(), _stream_ptr(stream)))
+            self._bws.data_ptr(), self._bws.numel(), _stream_ptr(stream, self._dev)))
         return {"dz": dz, "dW_mask": dW, "dx": dx, "d_gate": dg}
 
     def stats(self, counters: "RoutingStats", stream=None):
@@ -338,7 +348,8 @@ class RoutingStats:
         rs.mask, rs.masked_ids = R["mask"].data_ptr(), R["masked_ids"].data_ptr()
         _check(lib().beam_moe_stats(ctypes.byref(desc), ctypes.byref(rs),
                                     self.rank_masked.data_ptr(), self.active_hist.data_ptr(),
-                                    self.expert_load.data_ptr(), _stream_ptr(stream)))
+                                    self.expert_load.data_ptr(),
+                                    _stream_ptr(stream, self.expert_load.get_device())))
 
     def zero_(self):
         for t in (self.rank_masked, self.active_hist, self.expert_load):
@@ -362,7 +373,7 @@ def route(x, W_gate, W_mask, K, I, block_m=0, flags=0, tau=0.0, stream=None, n_s
     ws = torch.empty(max(sizes["route_workspace_bytes"], 256), dtype=torch.uint8, device=x.device)
     _check(lib().beam_moe_route(ctypes.byref(desc), x.data_ptr(), W_gate.data_ptr(),
                                 W_mask.data_ptr(), ctypes.byref(_routing_struct(R)),
-                                ws.data_ptr(), ws.numel(), _stream_ptr(stream)))
+                                ws.data_ptr(), ws.numel(), _stream_ptr(stream, x.get_device())))
     R["_ws"] = ws  # keep alive until the stream has used it
     R["_sizes"] = sizes
     return R
@@ -386,4 +397,5 @@ def forward_noalloc(desc: Desc, x, W_gate, W_mask, W_gu, W_dt, y, R: dict, strea
         _gpu_tensor(name, t)
     _check(lib().beam_moe_forward_noalloc(
         ctypes.byref(desc), x.data_ptr(), W_gate.data_ptr(), W_mask.data_ptr(), W_gu.data_ptr(),
-        W_dt.data_ptr(), y.data_ptr(), ctypes.byref(_routing_struct(R)), _stream_ptr(stream)))
+        W_dt.data_ptr(), y.data_ptr(), ctypes.byref(_routing_struct(R)),
+        _stream_ptr(stream, x.get_device())))

@@ -10,6 +10,7 @@
 //               layer, rounded to nearest even; float for the float layer)
 //   o [cap, d]  expert output per sorted position (same element type)
 // and the combine reads o through pair_pos[t*K + k] (-1 when masked).
+#include <algorithm>
 #include <mutex>
 
 #include "common.h"
@@ -199,19 +200,24 @@ static hipError_t launch_ring(const void *A, const void *W, const Plan &p, const
 
 // ---------------------------------------------------------------------------
 // Down projection and combine of a decode batch of at most SMALL_DECODE_T
-// tokens (Eq. 3 and Eq. 8), token-major: workgroup b owns token t = b / NG
-// and a range of C output channels.  The token's slots (its S shared experts
-// with weight 1, then its active routed slots k in order with weight g_hat)
-// and their h rows are staged in LDS.  The items (slot q, channel c) are
-// spread over the waves, eight at a time per wave with every row piece
-// requested before any arithmetic: each streams row c of the slot's W_dt
-// (16-byte loads), dots it with the slot's h row and sums the lanes in a
-// fixed order into o[q][c] in LDS.  Then each channel adds its slots in slot
-// order (float32, no atomics) and writes y[t][c].  With a few tokens the
-// experts' rows are read once per token that uses them, about once per
-// active expert.
+// tokens (Eq. 3 and Eq. 8), token-major: each workgroup owns one token t and
+// a range of C output channels.  With one token every workgroup takes it;
+// with more, the G workgroups are dealt out in proportion to the tokens' slot
+// counts n_t (the S shared experts plus the active routed slots): token t
+// gets 1 + floor((G - T) n_t / W) of them, W the sum of the n_t, so a token
+// with many active slots does not hold up the launch (with an equal share
+// per token its workgroups took several times as long as the others').  The
+// token's slots (its S shared experts with weight 1, then its active routed
+// slots k in order with weight g_hat) and their h rows are staged in LDS.
+// The items (slot q, channel c) are spread over the waves, eight at a time
+// per wave with every row piece requested before any arithmetic: each
+// streams row c of the slot's W_dt (16-byte loads), dots it with the slot's
+// h row and sums the lanes in a fixed order into o[q][c] in LDS.  Then each
+// channel adds its slots in slot order (float32, no atomics) and writes
+// y[t][c].  With a few tokens the experts' rows are read once per token that
+// uses them, about once per active expert.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(512) void down_small(int T, int K, int S, int E, int d, int I, int NG,
+__global__ __launch_bounds__(512) void down_small(int T, int K, int S, int E, int d, int I,
                                                   const int32_t *__restrict__ masked_ids,
                                                   const float *__restrict__ g_hat,
                                                   const int32_t *__restrict__ pair_pos,
@@ -220,13 +226,51 @@ __global__ __launch_bounds__(512) void down_small(int T, int K, int S, int E, in
                                                   bf16_t *__restrict__ y) {
     __shared__ int s_e[SMALL_SLOTS], s_pos[SMALL_SLOTS];
     __shared__ float s_w[SMALL_SLOTS];
-    __shared__ int s_n;
+    __shared__ int s_n, s_t, s_grp, s_ng;
     // [slots][I] bf16 h rows, then [slots][per] float slot outputs
     extern __shared__ __align__(16) unsigned char dyn[];
     u32x4 *hs = reinterpret_cast<u32x4 *>(dyn);
-    const int t = blockIdx.x / NG, grp = blockIdx.x - t * NG;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int per = (d + NG - 1) / NG;
+    const int G = gridDim.x;
+    int t = 0, grp = blockIdx.x, ng = G;
+    if (T > 1) {
+        if (tid < 64) {
+            // lane u < T: the active routed slots of token u (T * K <= 128)
+            int cnt = 0;
+            for (int c0 = 0; c0 < T * K; c0 += 64) {
+                const int l = c0 + lane;
+                const unsigned long long bal = __ballot(l < T * K && masked_ids[l] >= 0);
+                const int lo = max(lane * K - c0, 0), hi = min(lane * K + K - c0, 64);
+                if (lane < T && hi > lo)
+                    cnt += __popcll((bal >> lo) &
+                                    (hi - lo >= 64 ? ~0ull : (1ull << (hi - lo)) - 1ull));
+            }
+            int W = 0;
+            for (int u = 0; u < T; ++u) W += S + __builtin_amdgcn_readlane(cnt, u);
+            int first = 0, tt = -1, gg = 0, nn = 0;
+            for (int u = 0; u < T; ++u) {
+                const int n = S + __builtin_amdgcn_readlane(cnt, u);
+                const int g = 1 + (W > 0 ? (int)((long long)(G - T) * n / W) : 0);
+                if (tt < 0 && (int)blockIdx.x < first + g) {
+                    tt = u;
+                    gg = (int)blockIdx.x - first;
+                    nn = g;
+                }
+                first += g;
+            }
+            if (lane == 0) {
+                s_t = tt;
+                s_grp = gg;
+                s_ng = nn;
+            }
+        }
+        __syncthreads();
+        t = s_t;
+        grp = s_grp;
+        ng = s_ng;
+        if (t < 0) return;  // beyond the dealt workgroups (the whole workgroup)
+    }
+    const int per = (d + ng - 1) / ng;
     float *so = reinterpret_cast<float *>(dyn + (size_t)(K + S) * I * 2);
     if (tid < 64) {
         // lane l < S: shared expert l (weight 1); S <= l < S + K: routed slot
@@ -261,10 +305,13 @@ __global__ __launch_bounds__(512) void down_small(int T, int K, int S, int E, in
     const int C = c_end > c_begin ? c_end - c_begin : 0;
     const int n_items = n * C;
     constexpr int IU = 8;  // items per wave at a time
-    // every load is issued (past the end: item i0 / the row's first chunk
-    // again, in bounds and unused), so the compiler keeps all of them in
-    // flight; a batch's rows are requested before the previous batch's
-    // arithmetic (the first batch before the h rows are staged)
+    // wave w takes items i0 .. i0 + IU - 1, i0 = IU w + 8 IU j.  Every load is
+    // issued (past the end: item i0 / the row's first chunk again, in bounds
+    // and unused), so the compiler keeps all of them in flight; a batch's
+    // rows are requested before the previous batch's arithmetic (the first
+    // batch before the h rows are staged).  (Items dealt to the waves in turn
+    // instead were 0.7 us slower per layer call at one token: every wave
+    // then issues its IU row pieces for one or two real items.)
     const int ch0 = lane < nch ? lane : 0;
     const int ch1 = lane + 64 < nch ? lane + 64 : 0;
     u32x4 wv[IU][2];
@@ -272,10 +319,10 @@ __global__ __launch_bounds__(512) void down_small(int T, int K, int S, int E, in
     auto request = [&](int i0) {
 #pragma unroll
         for (int u = 0; u < IU; ++u) {
-            const int it = i0 + u < n_items ? i0 + u : (i0 < n_items ? i0 : 0);
-            qv[u] = C > 0 ? it / C : 0;
+            const int it = i0 + u < n_items ? i0 + u : i0;
+            qv[u] = it / C;
             cv[u] = c_begin + (it - qv[u] * C);
-            const bf16_t *wr = Wdt + ((size_t)s_e[qv[u]] * d + (cv[u] < d ? cv[u] : 0)) * I;
+            const bf16_t *wr = Wdt + ((size_t)s_e[qv[u]] * d + cv[u]) * I;
             wv[u][0] = ld16_stream(wr + (size_t)ch0 * 8);
             wv[u][1] = ld16_stream(wr + (size_t)ch1 * 8);
         }
@@ -323,17 +370,35 @@ __global__ __launch_bounds__(512) void down_small(int T, int K, int S, int E, in
     }
 }
 
+// LDS of down_small: the slots' h rows, and the slot outputs n_t x per_t.
+// One token: per = ceil(d / G).  More: n_t ceil(d / g_t) with
+// g_t = 1 + floor((G - T) n_t / W) > (G - T) n_t / W is below
+// d W / (G - T) + n_t <= d T (K + S) / (G - T) + K + S.
+static size_t down_small_lds(const Plan &p, int G) {
+    const long long slots = p.K + p.S;
+    const long long so = p.T == 1 ? slots * ((p.d + G - 1) / G)
+                                  : (long long)p.d * p.T * slots / (G - p.T) + slots + 1;
+    return (size_t)slots * p.I * 2 + (size_t)so * 4;
+}
+
 hipError_t launch_down_small(const Plan &p, const void *W_dt, const Routing &r, const Work &w,
                              void *y, hipStream_t s) {
-    // channel groups per token: about one workgroup per CU in all (two per
-    // CU measured 1-4 us slower at 1-2 tokens)
-    int ng = device_cus() / p.T;
-    ng = ng < 1 ? 1 : ng;
-    const int per = (p.d + ng - 1) / ng;
-    const size_t lds = (size_t)(p.K + p.S) * p.I * 2 + (size_t)(p.K + p.S) * per * 4;
-    down_small<<<p.T * ng, 512, lds, s>>>(p.T, p.K, p.S, p.E, p.d, p.I, ng, r.masked_ids,
-                                          r.g_hat, w.pair_pos, (const bf16_t *)w.h,
-                                          (const bf16_t *)W_dt, (bf16_t *)y);
+    // about one workgroup per CU in all (two per CU measured 1-4 us slower
+    // at 1-2 tokens); at least two per token
+    const int G = std::max(device_cus(), 2 * p.T);
+    const size_t lds = down_small_lds(p, G);
+    if (lds > 64 * 1024) {
+        static std::once_flag once;
+        static hipError_t attr_err = hipSuccess;
+        std::call_once(once, [] {
+            attr_err = hipFuncSetAttribute((const void *)down_small,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        });
+        if (attr_err != hipSuccess) return attr_err;
+    }
+    down_small<<<G, 512, lds, s>>>(p.T, p.K, p.S, p.E, p.d, p.I, r.masked_ids, r.g_hat,
+                                   w.pair_pos, (const bf16_t *)w.h, (const bf16_t *)W_dt,
+                                   (bf16_t *)y);
     return hipGetLastError();
 }
 

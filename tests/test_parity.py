@@ -89,6 +89,19 @@ def test_qwen3_decode(T, mode):
     _full_check(L, 8)
 
 
+# Small decode batches whose tokens have very different numbers of active
+# slots (skewed recipe: per-token mask biases +1 / -2 / -8, so some tokens
+# keep most slots and some none): the down kernel deals its workgroups to the
+# tokens in proportion to their slot counts.
+@pytest.mark.parametrize("T", [2, 3, 5, 8])
+def test_qwen3_small_batch_uneven_slots(T):
+    L = layer("qwen3", T, seed=650 + T, skew=True)
+    _, G, O, _ = _full_check(L, 8)
+    per_token = (np.asarray(O["masked_ids"]).reshape(T, 8) >= 0).sum(axis=1)
+    if T >= 5:
+        assert per_token.max() >= 4 and per_token.min() == 0, per_token
+
+
 @pytest.mark.parametrize("b", [-1.04, 8.0])
 def test_qwen3_prefill_2048(b):
     L = layer("qwen3", 2048, seed=700, mask_bias=b)

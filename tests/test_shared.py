@@ -55,6 +55,16 @@ def test_shared_bf16(name, T, b):
     _check(L, shape, S, T, 1e-2)
 
 
+@pytest.mark.parametrize("T", [2, 8])
+def test_shared_small_batch_uneven_slots(T):
+    # small decode batch, skewed per-token mask biases: the tokens' slot
+    # counts (2 shared + 0..6 routed) differ, and so do their down workgroups
+    need_gpu()
+    shape, S = synth.SHAPES["dsv2lite"], synth.N_SHARED["dsv2lite"]
+    L = _layer(shape, T, S, seed=2650 + T, skew=True)
+    _check(L, shape, S, T, 1e-2, n_sample=T)
+
+
 @pytest.mark.parametrize("T", [5, 300])
 def test_shared_tiled_forced(T):
     need_gpu()
