@@ -12,6 +12,7 @@
 // and the combine reads o through pair_pos[t*K + k] (-1 when masked).
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -304,61 +305,69 @@ __global__ __launch_bounds__(512) void down_small(int T, int K, int S, int E, in
     const int c_begin = grp * per, c_end = min(d, c_begin + per);
     const int C = c_end > c_begin ? c_end - c_begin : 0;
     const int n_items = n * C;
-    constexpr int IU = 8;  // items per wave at a time
-    // wave w takes items i0 .. i0 + IU - 1, i0 = IU w + 8 IU j.  Every load is
-    // issued (past the end: item i0 / the row's first chunk again, in bounds
-    // and unused), so the compiler keeps all of them in flight; a batch's
-    // rows are requested before the previous batch's arithmetic (the first
-    // batch before the h rows are staged).  (Items dealt to the waves in turn
-    // instead were 0.7 us slower per layer call at one token: every wave
-    // then issues its IU row pieces for one or two real items.)
+    // IU items per wave at a time, every row piece requested before any
+    // arithmetic; a batch's rows are requested before the previous batch's
+    // arithmetic (the first batch before the h rows are staged).  Many items:
+    // IU = 8 consecutive ones per wave (items i0 + u, i0 = 8 w + 64 j).  At
+    // most 16 (a token's few slots over a short channel range): IU = 2 dealt
+    // to the waves in turn (items i0 + 8 u, i0 = w + 16 j), so a wave issues
+    // row pieces for at most one missing item.  Every load is issued (past
+    // the end: item i0 / the row's first chunk again, in bounds and unused),
+    // so the compiler keeps all of them in flight.
     const int ch0 = lane < nch ? lane : 0;
     const int ch1 = lane + 64 < nch ? lane + 64 : 0;
-    u32x4 wv[IU][2];
-    int qv[IU], cv[IU];
-    auto request = [&](int i0) {
+    auto run = [&](auto IUC, auto STC) {
+        constexpr int IU = decltype(IUC)::value, ST = decltype(STC)::value;
+        u32x4 wv[IU][2];
+        int qv[IU], cv[IU];
+        auto request = [&](int i0) {
 #pragma unroll
-        for (int u = 0; u < IU; ++u) {
-            const int it = i0 + u < n_items ? i0 + u : i0;
-            qv[u] = it / C;
-            cv[u] = c_begin + (it - qv[u] * C);
-            const bf16_t *wr = Wdt + ((size_t)s_e[qv[u]] * d + cv[u]) * I;
-            wv[u][0] = ld16_stream(wr + (size_t)ch0 * 8);
-            wv[u][1] = ld16_stream(wr + (size_t)ch1 * 8);
+            for (int u = 0; u < IU; ++u) {
+                const int it = i0 + ST * u < n_items ? i0 + ST * u : i0;
+                qv[u] = it / C;
+                cv[u] = c_begin + (it - qv[u] * C);
+                const bf16_t *wr = Wdt + ((size_t)s_e[qv[u]] * d + cv[u]) * I;
+                wv[u][0] = ld16_stream(wr + (size_t)ch0 * 8);
+                wv[u][1] = ld16_stream(wr + (size_t)ch1 * 8);
+            }
+        };
+        int i0 = ST == 1 ? wave * IU : wave;
+        if (i0 < n_items) request(i0);
+        for (int i = tid; i < n * nch; i += 512) {
+            const int q = i / nch, ch = i - q * nch;
+            hs[i] = ld16(h + (size_t)s_pos[q] * I + (size_t)ch * 8);
+        }
+        __syncthreads();
+        for (; i0 < n_items; i0 += 8 * IU) {
+            u32x4 cur[IU][2];
+            int qc[IU], cc_[IU];
+#pragma unroll
+            for (int u = 0; u < IU; ++u) {
+                cur[u][0] = wv[u][0];
+                cur[u][1] = wv[u][1];
+                qc[u] = qv[u];
+                cc_[u] = cv[u];
+            }
+            if (i0 + 8 * IU < n_items) request(i0 + 8 * IU);
+#pragma unroll
+            for (int u = 0; u < IU; ++u) {
+                const int q = qc[u], c = cc_[u];
+                float part = 0.f;
+                if (lane < nch) part = dot8_bf16(cur[u][0], hs[q * nch + lane], part);
+                if (lane + 64 < nch) part = dot8_bf16(cur[u][1], hs[q * nch + lane + 64], part);
+                // a row longer than 128 chunks: the rest, one piece at a time
+                const bf16_t *wr = Wdt + ((size_t)s_e[q] * d + c) * I;
+                for (int ch = lane + 128; ch < nch; ch += 64)
+                    part = dot8_bf16(ld16_stream(wr + (size_t)ch * 8), hs[q * nch + ch], part);
+                const float o = wave_sum(part);
+                if (lane == 0 && i0 + ST * u < n_items) so[q * per + (c - c_begin)] = o;
+            }
         }
     };
-    int i0 = wave * IU;
-    if (i0 < n_items) request(i0);
-    for (int i = tid; i < n * nch; i += 512) {
-        const int q = i / nch, ch = i - q * nch;
-        hs[i] = ld16(h + (size_t)s_pos[q] * I + (size_t)ch * 8);
-    }
-    __syncthreads();
-    for (; i0 < n_items; i0 += 8 * IU) {
-        u32x4 cur[IU][2];
-        int qc[IU], cc_[IU];
-#pragma unroll
-        for (int u = 0; u < IU; ++u) {
-            cur[u][0] = wv[u][0];
-            cur[u][1] = wv[u][1];
-            qc[u] = qv[u];
-            cc_[u] = cv[u];
-        }
-        if (i0 + 8 * IU < n_items) request(i0 + 8 * IU);
-#pragma unroll
-        for (int u = 0; u < IU; ++u) {
-            const int q = qc[u], c = cc_[u];
-            float part = 0.f;
-            if (lane < nch) part = dot8_bf16(cur[u][0], hs[q * nch + lane], part);
-            if (lane + 64 < nch) part = dot8_bf16(cur[u][1], hs[q * nch + lane + 64], part);
-            // a row longer than 128 chunks: the rest, one piece at a time
-            const bf16_t *wr = Wdt + ((size_t)s_e[q] * d + c) * I;
-            for (int ch = lane + 128; ch < nch; ch += 64)
-                part = dot8_bf16(ld16_stream(wr + (size_t)ch * 8), hs[q * nch + ch], part);
-            const float o = wave_sum(part);
-            if (lane == 0 && i0 + u < n_items) so[q * per + (c - c_begin)] = o;
-        }
-    }
+    if (n_items <= 16)
+        run(std::integral_constant<int, 2>{}, std::integral_constant<int, 8>{});
+    else
+        run(std::integral_constant<int, 8>{}, std::integral_constant<int, 1>{});
     __syncthreads();
     for (int cc = tid; cc < C; cc += 512) {
         float acc = 0.f;
