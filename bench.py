@@ -19,7 +19,8 @@ the whole-layer HBM fraction, this GPU's measured copy/read bandwidth and
 bf16 MFMA rate, the same kernels with the mask forced all-ones (W_mask = 0,
 plain Top-K), a sweep over the decode batch sizes, the prefill runs (keep
 0.15 / 0.3 / 0.5 / 1.0 at T = 2048 and 8192, and the skewed T = 16384 load),
-a stack of 48 distinct layers at T = 64 under the skewed load (eager and as
+the vendor GEMM (hipBLASLt through torch) on the same expert GEMM shapes as
+context for the prefill MFMA figures, a stack of 48 distinct layers at T = 64 under the skewed load (eager and as
 one replayed HIP graph; also at T = 1 and 8), a DeepSeekV2-Lite-shaped layer with two always-on
 shared experts (decode, masked and all-ones), the mask-router backward
 (straight-through estimator + sparsity term), the d=4096/I=1536 layer (decode T = 1 and 64,
@@ -97,6 +98,10 @@ def parse():
     ap.add_argument("--shared", action="store_true", default=True,
                     help="also measure the DeepSeekV2-Lite-shaped layer with 2 shared experts")
     ap.add_argument("--no-shared", dest="shared", action="store_false")
+    ap.add_argument("--vendor-gemm", action="store_true", default=True,
+                    help="also time the vendor GEMM (torch.bmm / matmul, hipBLASLt) on the "
+                         "expert GEMM shapes of the T=8192 keep-1.0 prefill layer")
+    ap.add_argument("--no-vendor-gemm", dest="vendor_gemm", action="store_false")
     ap.add_argument("--large", action="store_true", default=True,
                     help="also measure the d=4096/I=1536 layer (decode T=1, 64; prefill 4096)")
     ap.add_argument("--no-large", dest="large", action="store_false")
@@ -483,6 +488,9 @@ def main():
         backward = run_backward(B, sets, shape, dev)
 
     prefill_out = [] if args.only_headline else run_prefill()
+    vendor = None
+    if args.vendor_gemm and not args.only_headline:
+        vendor = run_vendor_gemm(dev, shape)
 
     # ---- CPU baseline: the fp64 oracle on this host's cores ---------------
     cpu = None
@@ -530,6 +538,7 @@ def main():
             "speedup_masked_vs_allones": round(ones["ms_per_step"] / head["ms_per_step"], 3)},
         "sweep": sweep_out,
         "prefill": prefill_out,
+        "vendor_gemm": vendor,
         "stack": stack,
         "stack_small": stack_small,
         "shared": shared,
@@ -609,6 +618,61 @@ def run_stack(B, synth, sets, shape, dev, T, steps, dims):
            "active_experts_per_layer": round(sum(acts) / n, 2),
            "bytes_per_step": byts, "eager": eager, "graph": graph}
     del g, Ls
+    return out
+
+
+def run_vendor_gemm(dev, shape, reps=20):
+    """Context for the prefill MFMA figures: the vendor library's bf16 GEMM
+    (torch.bmm / torch.matmul, hipBLASLt) on the expert GEMMs of the T=8192
+    keep-1.0 layer (E experts x 8192 K / E rows each, up [rows, d] x [d, 2I],
+    down [rows, I] x [I, d]), as one batched call and as one dense GEMM over
+    all rows, plus a square 8192^3 GEMM.  Operands are random and contiguous
+    (no transposed views)."""
+    import torch
+
+    E, d, I = shape.E, shape.d, shape.I
+    M = 8192 * shape.K // E
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    bf = torch.bfloat16
+    rnd = lambda *sz: torch.randn(*sz, generator=g, device=dev, dtype=torch.float32).to(bf)  # noqa: E731
+
+    def timeit(f, flops):
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            f()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        tf = flops / (ms * 1e-3) / 1e12
+        return {"us": round(ms * 1e3, 1), "TFLOPs": round(tf, 1),
+                "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+
+    out = {"library": "torch.bmm / torch.matmul (hipBLASLt), bf16", "rows_per_expert": M}
+    A = rnd(E, M, d)
+    Wu = rnd(E, d, 2 * I)
+    out["bmm_up"] = timeit(lambda: torch.bmm(A, Wu), 2.0 * E * M * d * 2 * I)
+    W1 = Wu[0].contiguous()
+    A2 = A.reshape(E * M, d)
+    out["dense_up"] = timeit(lambda: A2 @ W1, 2.0 * E * M * d * 2 * I)
+    del Wu, W1, A, A2
+    H = rnd(E, M, I)
+    Wd = rnd(E, I, d)
+    out["bmm_down"] = timeit(lambda: torch.bmm(H, Wd), 2.0 * E * M * I * d)
+    W2 = Wd[0].contiguous()
+    H2 = H.reshape(E * M, I)
+    out["dense_down"] = timeit(lambda: H2 @ W2, 2.0 * E * M * I * d)
+    del H, Wd, W2, H2
+    X, Y = rnd(8192, 8192), rnd(8192, 8192)
+    out["square_8192"] = timeit(lambda: X @ Y, 2.0 * 8192 ** 3)
+    del X, Y
+    torch.cuda.empty_cache()
+    log("vendor GEMM: " + ", ".join(f"{k} {v['us']} us ({v['mfma_frac']:.3f})"
+                                    for k, v in out.items() if isinstance(v, dict)))
     return out
 
 
