@@ -417,12 +417,13 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
 
     // epilogue: D[i][j] of a 32x32 tile sits in lane j + 32*((i/4) % 2),
     // register 4*(i/8) + i%4.  Pad rows of a block compute values nothing
-    // reads (their A rows are token 0 / h rows inside the buffer).  A wave's
-    // rows lie wholly inside or wholly past the segment (segments are
-    // multiples of 128 rows, wave rows WT <= 64 aligned), so each wave
-    // issues all of its C::ST stores or none.
+    // reads (their A rows are token 0 / h rows inside the buffer).  A wave
+    // whose rows are all pad (or the next expert's) stores nothing: no
+    // pair's result lives there, and the down GEMM does not load h rows of
+    // an 8-row group that lies wholly past the valid rows.  Every other
+    // wave issues all of its C::ST stores.
     auto epilogue = [&](const Tile &t) {
-        if (wm * WT >= t.seg) return;  // the next expert's rows
+        if (wm * WT >= t.rows_valid) return;  // pad rows only
 #pragma unroll
         for (int m = 0; m < MF; ++m) {
 #pragma unroll
@@ -478,7 +479,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
         }
         epilogue(cur);
         if (!more) break;
-        stores = wm * WT >= cur.seg ? 0 : 1;
+        stores = wm * WT >= cur.rows_valid ? 0 : 1;
         cur = nxt;
         tile = next;
     }
