@@ -3,7 +3,8 @@
 The compute lives in the HIP library libbeam_moe.so (C-ABI declared in
 include/beam_moe.h).  This module only marshals torch tensors into that
 library's calls: it allocates outputs and workspace with torch, passes their
-device pointers and torch's current stream, and returns the tensors.  There is
+device pointers and torch's current stream of the tensors' GPU (or the stream
+a call names), and returns the tensors.  There is
 no CPU fallback: every call raises if the library is missing or the tensors
 are not on a GPU.
 """

@@ -245,9 +245,11 @@ __global__ __launch_bounds__(256) void router_logits_generic(
 // ---------------------------------------------------------------------------
 // Select (Eq. 4-7 per token).  A token is handled by the 16 lanes of one DPP
 // row of a wavefront; lane i of the row holds the gate logits of experts
-// i*EJ .. i*EJ+EJ-1, so a wavefront handles 4 consecutive tokens.  K rounds
-// of a row-wide arg-max under the key (value desc, expert asc) give the Top-K
-// slots in order (Eq. 4); slot k (K <= 16) is kept by lane k.  Softmax over the kept logits shifted by the largest
+// i*EJ .. i*EJ+EJ-1, so a wavefront handles 4 consecutive tokens.  Each lane
+// sorts its EJ candidates once; then K rounds take the row-wide maximum of the
+// lanes' best remaining candidates under the order (value desc, expert asc),
+// which gives the Top-K slots in order (Eq. 4); slot k (K <= 16) is kept by
+// lane k.  Softmax over the kept logits shifted by the largest
 // (Eq. 4); the winners' mask logits are gathered afterwards and m = z >= thr
 // (Eq. 6, thr = 0 for tau = 0.5); g_hat = g * m (Eq. 7); id -1 where masked.
 // tmask[e] collects the set of tokens with an active pair for expert e, bit
@@ -379,8 +381,9 @@ __device__ __forceinline__ void select_group(
     unsigned long long top = 0ull, kept = 0ull;
     for (int k = 0; k < K; ++k) {
         const unsigned long long b = row_max_key(key[0]);
-        // all ones in the lane that held the head: a bit-select per word
-        // (v_bfi_b32) moves its list up
+        // all ones in the lane that held the head, whose list then moves up
+        // by a select per word (written with masks: the compiler turned the
+        // plain conditional copies into a chain of index compares)
         const unsigned long long m = 0ull - (unsigned long long)(key[0] == b);
 #pragma unroll
         for (int j = 0; j + 1 < EJ; ++j) key[j] = (key[j + 1] & m) | (key[j] & ~m);
