@@ -61,3 +61,50 @@ def test_random_shape(d, E, K, I, S, T, tau, bias, flags, fp32):
         assert np.all(G["counts"][E:] == T)
     check_y(y.float().cpu().numpy(), L, K, O, 1e-5 if fp32 else 1e-2,
             tokens=sample_tokens(T, 24, seed=seed))
+
+
+# Small decode batches (T <= 8 tokens, bf16): the three-launch path, whose
+# every workgroup routes the batch itself (select over 1-16 experts per lane,
+# E not a multiple of 16, shared experts) and whose down kernel deals its
+# workgroups to the tokens by their slot counts (uniform or per-token mask
+# biases).
+def _draw_small_cases(n, seed=20261204):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        d = int(rng.choice([128, 256, 384, 640, 2048]))
+        E = int(rng.integers(2, 257))
+        K = int(rng.integers(1, min(16, E) + 1))
+        S = int(rng.choice([0, 0, 1, 2, 4]))
+        I = int(rng.choice([64, 128, 192, 320, 768]))
+        T = int(rng.integers(1, 9))
+        if E + S > 256 or (K + S) * I * 2 > 48 * 1024:
+            continue
+        skew = bool(rng.random() < 0.4) and d >= 2
+        bias = float(rng.choice([-1.0, 0.0, 0.5]))
+        cases.append((d, E, K, I, S, T, bias, skew))
+    return cases
+
+
+SMALL_CASES = _draw_small_cases(16)
+
+
+@pytest.mark.parametrize("d,E,K,I,S,T,bias,skew", SMALL_CASES,
+                         ids=[f"d{c[0]}-E{c[1]}-K{c[2]}-I{c[3]}-S{c[4]}-T{c[5]}-b{c[6]}"
+                              f"{'-skew' if c[7] else ''}" for c in SMALL_CASES])
+def test_random_small_batch(d, E, K, I, S, T, bias, skew):
+    need_gpu()
+    shape = synth.LayerShape(d, E, K, I, torch.bfloat16)
+    seed = 5000 + d + 7 * E + 13 * K + I + 17 * S + T
+    kw = {"skew": True} if skew else {"mask_bias": bias}
+    L = synth.make_layer(shape, T, seed=seed, n_shared=S, device="cuda", **kw)
+    W_gu, W_dt = L["W_gu"], L["W_dt"]
+    if S:
+        W_gu = torch.cat([W_gu, L["Ws_gu"]]).contiguous()
+        W_dt = torch.cat([W_dt, L["Ws_dt"]]).contiguous()
+    lay = B.MoELayer(L["W_gate"], L["W_mask"], W_gu, W_dt, K)
+    y, R = lay(L["x"])
+    torch.cuda.synchronize()
+    G = gpu_routing_host({k: v.cpu() for k, v in R.items()})
+    O = check_routing_exact(G, K, lay.sizes["block_m"], 0.5, n_shared=S)
+    check_y(y.float().cpu().numpy(), L, K, O, 1e-2)
