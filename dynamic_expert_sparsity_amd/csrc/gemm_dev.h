@@ -54,9 +54,12 @@ constexpr int GBN = 256;   // output columns per tile
 constexpr int GBK = 64;    // k per stage: one 128-byte line per row
 constexpr int G_ROWB = GBK * 2;       // bytes per row per stage
 constexpr int G_RPI = 1024 / G_ROWB;  // rows per 1 KB wave load (8)
-// k-slices (of 4) over which a stage's loads are spread in the expert GEMMs
+// k-slices (of 4) over which a stage's loads are spread in the 256-row
+// tiles: the first two, so the A loads of the next stage go out at the start
+// of a stage and have all of it to land (against all four: 1-2% faster up
+// projections at keep 0.5-1.0, A/B in both orders)
 #ifndef G_DKK
-#define G_DKK 4
+#define G_DKK 2
 #endif
 #ifndef G_SKIP_A
 #define G_SKIP_A 1
