@@ -58,40 +58,70 @@ __global__ __launch_bounds__(256) void compact_bases(const uint64_t *__restrict_
 }
 
 // One thread per pair, after the offsets (recomputed in every workgroup from
-// cnt; only workgroup 0 writes them out, so no workgroup reads another's
-// writes).
+// the counts; only workgroup 0 writes them out, so no workgroup reads
+// another's writes).  SELF (at most SCATTER_SELF_TILES tiles): every
+// workgroup also makes the counts and the per-tile bases itself, in LDS,
+// from the tile words (thread e reads expert e's word of every tile at
+// once), so compact_bases does not run; at 2048 tokens that launch cost
+// more than the 32 words per expert it spares each workgroup.
+template <bool SELF>
 __global__ __launch_bounds__(256) void compact_scatter(
     Routing r, const int32_t *__restrict__ cnt, int bm, int split, int32_t *__restrict__ meta,
     int32_t *__restrict__ pbt, const int32_t *__restrict__ tile_base,
-    const uint64_t *__restrict__ tile_mask, int PT, int TK, int K, int E, int S,
+    const uint64_t *__restrict__ tile_mask, int n_tiles, int PT, int TK, int K, int E, int S,
     int32_t *__restrict__ pair_pos, int32_t *__restrict__ sorted_tok) {
     __shared__ int s_cnt[256];
     __shared__ int s_off[257];
+    __shared__ int32_t s_tb[SELF ? SCATTER_SELF_TILES * 256 : 1];
     const int E2 = E + S;
     const int tid = threadIdx.x;
     const int p = blockIdx.x * 256 + tid;
     // the pair's masked id is requested before the offsets are made
     const int mid = p < TK ? r.masked_ids[p] : -1;
-    if (tid < E2) s_cnt[tid] = cnt[tid];
+    if (SELF) {
+        if (tid < E2) {
+            uint64_t wv[SCATTER_SELF_TILES];
+#pragma unroll
+            for (int t = 0; t < SCATTER_SELF_TILES; ++t)  // past n_tiles: tile 0 again, unused
+                wv[t] = tile_mask[(size_t)(t < n_tiles ? t : 0) * E2 + tid];
+            int base = 0;
+#pragma unroll
+            for (int t = 0; t < SCATTER_SELF_TILES; ++t) {
+                if (t < n_tiles) {
+                    s_tb[t * E2 + tid] = base;
+                    base += __popcll(wv[t]);
+                }
+            }
+            s_cnt[tid] = base;
+        }
+    } else {
+        if (tid < E2) s_cnt[tid] = cnt[tid];
+    }
     __syncthreads();
     if (tid < 64)
         offsets_from_counts(s_cnt, s_off, E2, bm, r, meta, pbt, split, tid, blockIdx.x == 0);
     __syncthreads();
     blocks_and_pads(s_off, s_cnt, E2, bm, PT, r, sorted_tok, p, gridDim.x * 256);
     if (p < PT)
-        scatter_pair(p, mid, K, TK, E, S, r, s_off, tile_base, tile_mask, pair_pos, sorted_tok);
+        scatter_pair(p, mid, K, TK, E, S, r, s_off, SELF ? s_tb : tile_base, tile_mask, pair_pos,
+                     sorted_tok);
 }
 
 hipError_t launch_scatter(const Plan &p, const Routing &r, const Work &w, hipStream_t s) {
     if (p.fuse_scatter) return hipSuccess;
-    compact_scatter<<<(p.PT + 255) / 256, 256, 0, s>>>(r, w.cnt, p.bm, p.split, w.meta, w.pbt,
-                                                       w.tile_base, w.tile_mask, p.PT,
-                                                       p.T * p.K, p.K, p.E, p.S, w.pair_pos,
-                                                       w.sorted_tok);
+    if (p.n_tiles <= SCATTER_SELF_TILES)
+        compact_scatter<true><<<(p.PT + 255) / 256, 256, 0, s>>>(
+            r, w.cnt, p.bm, p.split, w.meta, w.pbt, w.tile_base, w.tile_mask, p.n_tiles, p.PT,
+            p.T * p.K, p.K, p.E, p.S, w.pair_pos, w.sorted_tok);
+    else
+        compact_scatter<false><<<(p.PT + 255) / 256, 256, 0, s>>>(
+            r, w.cnt, p.bm, p.split, w.meta, w.pbt, w.tile_base, w.tile_mask, p.n_tiles, p.PT,
+            p.T * p.K, p.K, p.E, p.S, w.pair_pos, w.sorted_tok);
     return hipGetLastError();
 }
 
 hipError_t launch_bases(const Plan &p, const Work &w, hipStream_t s) {
+    if (p.n_tiles <= SCATTER_SELF_TILES) return hipSuccess;  // the scatter makes them
     compact_bases<<<(p.E2 + 3) / 4, 256, 0, s>>>(w.tile_mask, p.n_tiles, p.E2, w.tile_base,
                                                  w.cnt);
     return hipGetLastError();

@@ -11,6 +11,9 @@ namespace beam {
 constexpr int SMALL_DECODE_T = 8;
 // slots per token the small-batch down kernel holds in LDS (K + S)
 constexpr int SMALL_SLOTS = 32;
+// batches of more than 16 and at most this many select tiles (64 tokens
+// each): the pair-scatter workgroups make the per-tile bases themselves
+constexpr int SCATTER_SELF_TILES = 32;
 
 // Everything the launchers need, fixed on the host from the descriptor.
 struct Plan {
