@@ -128,7 +128,7 @@ int make_plan(const beam_moe_desc *desc, Plan &p) {
               (long long)(D.K + D.n_shared) * D.I * 2 <= 48 * 1024;
     p.s_ts = 64;
     p.n_tiles = (D.T + 63) / 64;
-    p.fuse_scatter = p.n_tiles <= 16;
+    p.fuse_scatter = D.T <= ROUTE_SMALL_T;
     p.max_active = (int)(PT < p.E2 ? PT : p.E2);
     // the streaming kernels number their units (position blocks of <= 32 x
     // column groups of 16 units up / 32 channels down) in int

@@ -1,5 +1,6 @@
-// a4 for batches of more than 16 select tiles: the grouping in two launches
-// of many workgroups (see compact_dev.h for the arithmetic).
+// a4 for batches of more than one select tile (64 tokens): the grouping in
+// one or two launches of many workgroups (see compact_dev.h for the
+// arithmetic).
 //   compact_bases:   per expert, the running count of its tokens over the
 //                    tiles (tile_base[tile][e]) and its total (cnt[e]);
 //   compact_scatter: every workgroup turns the totals into the block-padded
@@ -7,9 +8,11 @@
 //                    the routing records and the call's kernel record), then
 //                    takes its share of the block -> expert map and the pad
 //                    entries, and places its pairs.
-// A single workgroup did the first step and the offsets, block map and pads
-// (9.4 us at 8192 tokens, its steps one after another); spread out, the
-// serial part left is one wave's prefix sums per workgroup.
+// Up to SCATTER_SELF_TILES tiles compact_bases does not run: every scatter
+// workgroup makes the bases it needs itself.  A single workgroup did the
+// first step and the offsets, block map and pads (9.4 us at 8192 tokens, its
+// steps one after another); spread out, the serial part left is one wave's
+// prefix sums per workgroup.
 #include "compact_dev.h"
 
 namespace beam {

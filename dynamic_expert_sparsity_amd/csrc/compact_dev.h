@@ -218,81 +218,4 @@ __device__ __forceinline__ void scatter_pair(int p, int mid, int K, int TK, int 
     place_pair(p, t, off[e] + tile_base[qi] + rank, r, pair_pos, sorted_tok);
 }
 
-// Whole-batch compaction of at most 16 select tiles by one workgroup of
-// `nthreads` (>= E + S) threads, over the E routed and S shared experts
-// (E2 = E + S; tile token sets [n_tiles][E2]).  Thread (g, e), g = tid / E2,
-// sums the popcounts of a contiguous range of tiles for expert e; group
-// partials give every (tile, expert) its base; wave 0 scans the experts into
-// block-padded offsets; then the block map and pads, and the position of
-// every pair.  The tile words and bases stay in LDS (s_words, s_tb:
-// [n_tiles][E2]) for the placement, which then reads no global memory but
-// the masked ids, the first PRE of which per thread are requested before
-// anything else.  LDS: s_part[nthreads], s_cnt[256], s_off[257].  (Larger
-// batches use compact_bases and compact_scatter, many workgroups each.)
-__device__ __forceinline__ void scan_tiles(const uint64_t *tile_mask, int n_tiles, int Er, int S,
-                                           int bm, int K, int TK, const Routing &r,
-                                           int32_t *pair_pos, int32_t *meta, int32_t *sorted_tok,
-                                           int32_t *pbt, int split, int tid, int nthreads,
-                                           int *s_part, int *s_cnt, int *s_off, uint64_t *s_words,
-                                           int32_t *s_tb) {
-    const int E = Er + S;
-    const int PT = TK + (TK / K) * S;
-    const int NG = nthreads / E;
-    const int g = tid / E;
-    const int e = tid - g * E;
-    const bool on = g < NG;
-    const int chunk = (n_tiles + NG - 1) / NG;
-    const int tb = g * chunk;
-    const int te = min(n_tiles, tb + chunk);
-    constexpr int PRE = 4;  // masked ids requested up front per thread
-    int mid_pre[PRE];
-#pragma unroll
-    for (int j = 0; j < PRE; ++j) {
-        const int p = tid + j * nthreads;
-        mid_pre[j] = p < TK ? r.masked_ids[p] : -1;
-    }
-
-    int local = 0;
-    if (on) {
-        for (int t = tb; t < te; ++t) {
-            const uint64_t w = tile_mask[(size_t)t * E + e];
-            s_words[t * E + e] = w;
-            local += __popcll(w);
-        }
-    }
-    s_part[tid] = local;
-    __syncthreads();
-    if (on) {
-        int base = 0, total = 0;
-        for (int q = 0; q < NG; ++q) {
-            const int v = s_part[q * E + e];
-            if (q < g) base += v;
-            total += v;
-        }
-        for (int t = tb; t < te; ++t) {
-            s_tb[t * E + e] = base;
-            base += __popcll(s_words[t * E + e]);
-        }
-        if (g == 0) s_cnt[e] = total;
-    }
-    __syncthreads();
-    if (tid < 64) offsets_from_counts(s_cnt, s_off, E, bm, r, meta, pbt, split, tid);
-    __syncthreads();
-    blocks_and_pads(s_off, s_cnt, E, bm, PT, r, sorted_tok, tid, nthreads);
-    // s_words / s_tb were written before the last two barriers
-    for (int j = 0, p = tid; p < PT; ++j, p += nthreads) {
-        int mid = -1;
-        if (p < TK) {
-            if (j >= PRE) {
-                mid = r.masked_ids[p];
-            } else {
-#pragma unroll
-                for (int i = 0; i < PRE; ++i)
-                    if (j == i) mid = mid_pre[i];
-            }
-        }
-        scatter_pair(p, mid, K, TK, Er, S, r, s_off, s_tb, s_words, pair_pos, sorted_tok);
-    }
-}
-
 }  // namespace beam

@@ -11,8 +11,12 @@ namespace beam {
 constexpr int SMALL_DECODE_T = 8;
 // slots per token the small-batch down kernel holds in LDS (K + S)
 constexpr int SMALL_SLOTS = 32;
-// batches of more than 16 and at most this many select tiles (64 tokens
-// each): the pair-scatter workgroups make the per-tile bases themselves
+// batches of at most this many tokens (one 64-token select tile) are routed
+// and grouped by one workgroup (route_small)
+constexpr int ROUTE_SMALL_T = 64;
+static_assert(ROUTE_SMALL_T <= 64, "route_small holds one 64-token tile");
+// larger batches of at most this many select tiles (64 tokens each): the
+// pair-scatter workgroups make the per-tile bases themselves
 constexpr int SCATTER_SELF_TILES = 32;
 
 // Everything the launchers need, fixed on the host from the descriptor.
@@ -34,7 +38,7 @@ struct Plan {
     // select / compaction
     int s_ts;           // tokens per select tile (64)
     int n_tiles;        // ceil(T / s_ts)
-    int fuse_scatter;   // T <= 1024: the compaction workgroup also places the pairs
+    int fuse_scatter;   // T <= ROUTE_SMALL_T: the routing workgroup also places the pairs
     int small;          // bf16 decode batch of <= SMALL_DECODE_T tokens: up_small / down_small
     long long cap;          // sorted_pairs capacity
     long long n_blocks_cap; // block_expert capacity
@@ -59,7 +63,7 @@ struct Routing {
 struct Work {  // workspace views
     uint64_t *tile_mask;
     int32_t *tile_base;
-    int32_t *cnt;        // [E + S] per-expert active-pair counts (batches of > 16 tiles)
+    int32_t *cnt;        // [E + S] per-expert active-pair counts (batches of > 32 tiles)
     int32_t *pair_pos;   // [T*K] sorted position of each pair, -1 if masked
     int32_t *meta;       // [4] the call's record {mode (1 tiled, 0 streaming),
                          // max count, position blocks, 0}
@@ -77,9 +81,10 @@ hipError_t launch_router_logits(const Plan &p, const void *x, const void *Wg, co
                                 const Routing &r, hipStream_t s);
 hipError_t launch_route(const Plan &p, const void *x, const void *Wg, const void *Wm,
                         const Routing &r, const Work &w, hipStream_t s);
-// batches of more than 16 tiles: per-expert tile bases and counts (after the
-// select), then offsets and the pair scatter (a no-op for smaller batches,
-// whose routing kernel placed the pairs)
+// batches of more than ROUTE_SMALL_T tokens: per-expert tile bases and
+// counts after the select (more than SCATTER_SELF_TILES tiles; else the
+// scatter makes them), then offsets and the pair scatter (a no-op for
+// smaller batches, whose routing workgroup placed the pairs)
 hipError_t launch_bases(const Plan &p, const Work &w, hipStream_t s);
 hipError_t launch_scatter(const Plan &p, const Routing &r, const Work &w, hipStream_t s);
 // the tiled path (bf16): one launch per projection runs the kernel family

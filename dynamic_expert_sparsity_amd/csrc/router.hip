@@ -447,25 +447,6 @@ __global__ __launch_bounds__(256) void select_topk_mask(int T, int E, int S, int
         dst[4 * e] = (uint16_t)(e < E ? tmask[e] : tile_all(tile, T) >> (16 * q));
 }
 
-// The grouping of a batch of at most 16 tiles by one workgroup, the pairs
-// placed here too (larger batches: compact_bases after the select,
-// compact_scatter as the next stage).
-__global__ __launch_bounds__(1024) void compact_tiles(const uint64_t *__restrict__ tile_mask,
-                                                      int n_tiles, int E, int S, int bm, int K,
-                                                      int TK, Routing r,
-                                                      int32_t *__restrict__ pair_pos,
-                                                      int32_t *__restrict__ meta,
-                                                      int32_t *__restrict__ sorted_tok,
-                                                      int32_t *__restrict__ pbt, int split) {
-    __shared__ int s_part[1024];
-    __shared__ int s_cnt[256];
-    __shared__ int s_off[257];
-    __shared__ uint64_t s_words[16 * 256];
-    __shared__ int32_t s_tb[16 * 256];
-    scan_tiles(tile_mask, n_tiles, E, S, bm, K, TK, r, pair_pos, meta, sorted_tok, pbt, split,
-               threadIdx.x, 1024, s_part, s_cnt, s_off, s_words, s_tb);
-}
-
 // The routing of a small batch (T <= 64, one tile) by one workgroup of
 // nthreads threads (>= 256, a multiple of 64): select, counts, offsets,
 // lists and pair positions of the E routed and S shared experts; the token
@@ -735,28 +716,22 @@ hipError_t launch_up_small(const Plan &p, const void *x, const void *W_gu, const
     return hipGetLastError();
 }
 
-// A batch of at most BEAM_SMALL_T tokens (one 64-token tile) is routed by
-// one workgroup; a larger one by quarter-tile select workgroups and one
-// grouping workgroup.
-#ifndef BEAM_SMALL_T
-#define BEAM_SMALL_T 64
-#endif
-static_assert(BEAM_SMALL_T <= 64, "route_small holds one 64-token tile");
+// A batch of at most ROUTE_SMALL_T tokens (one 64-token tile) is routed by
+// one workgroup; a larger one by quarter-tile select workgroups, then (more
+// than SCATTER_SELF_TILES tiles) compact_bases, then the pair-scatter
+// workgroups.  (One grouping workgroup for up to 16 tiles was 2-8 us slower
+// per layer call at 128-1024 tokens than the scatter workgroups making the
+// bases themselves.)
 
 template <int EJ>
 static void launch_select_t(const Plan &p, const Routing &r, const Work &w, hipStream_t s) {
-    if (p.T <= BEAM_SMALL_T) {
+    if (p.T <= ROUTE_SMALL_T) {
         route_small<EJ><<<1, 1024, 0, s>>>(p.T, p.E, p.S, p.K, p.thr, p.bm, r, w.pair_pos, w.meta,
                                            w.sorted_tok, w.pbt, p.split);
     } else {
         select_topk_mask<EJ><<<p.n_tiles * 4, 256, 0, s>>>(p.T, p.E, p.S, p.K, p.thr, r,
                                                           w.tile_mask);
-        if (!p.fuse_scatter)  // more than 16 tiles: bases here, offsets with the scatter
-            launch_bases(p, w, s);
-        else
-            compact_tiles<<<1, 1024, 0, s>>>(w.tile_mask, p.n_tiles, p.E, p.S, p.bm, p.K,
-                                             p.T * p.K, r, w.pair_pos, w.meta, w.sorted_tok,
-                                             w.pbt, p.split);
+        launch_bases(p, w, s);  // (a no-op up to SCATTER_SELF_TILES tiles)
     }
 }
 

@@ -84,7 +84,7 @@ extern "C" {
                                  of at most 8 tokens: the logits only)            */
 #define BEAM_STAGE_SELECT   1 /* (inside BEAM_STAGE_ROUTER: empty)                */
 #define BEAM_STAGE_SCAN     2 /* (inside BEAM_STAGE_ROUTER: empty)                */
-#define BEAM_STAGE_SCATTER  3 /* a4: pairs into per-expert lists, T > 1024 only   */
+#define BEAM_STAGE_SCATTER  3 /* a4: pairs into per-expert lists, T > 64 only     */
 #define BEAM_STAGE_UP       4 /* a5: expert gate/up projections + SiLU * up       */
 #define BEAM_STAGE_DOWN     5 /* a6: expert down projection                       */
 #define BEAM_STAGE_COMBINE  6 /* a7: masked weighted sum                          */
