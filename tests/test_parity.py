@@ -14,6 +14,7 @@ import pytest
 import torch
 
 import oracle
+import dynamic_expert_sparsity_amd as B
 from dynamic_expert_sparsity_amd import synth
 from beamtest import (check_logits, check_routing_exact, check_y, gpu_routing_host, host, layer,
                       mode_record, need_gpu, run, sample_tokens)
@@ -52,6 +53,29 @@ SMALL = synth.LayerShape(128, 8, 2, 64, torch.bfloat16)
 def test_small_bf16_tokens(T):
     L = layer(SMALL, T, seed=200 + T, mask_bias=0.0)
     _full_check(L, 2)
+
+
+# Grouping at the batch sizes where its launches change: one routing
+# workgroup up to 64 tokens, then the pair-scatter workgroups making their own
+# tile bases up to 32 tiles (2048 tokens), then compact_bases first.  Shared
+# experts ride along (the tile words of experts E..E+S-1 are full).
+MID = synth.LayerShape(256, 48, 6, 128, torch.bfloat16)
+
+
+@pytest.mark.parametrize("T", [64, 65, 128, 1024, 1025, 2048, 2049, 2113])
+def test_grouping_launch_boundaries(T):
+    need_gpu()
+    L = layer(MID, T, seed=230 + T, mask_bias=-0.3, n_shared=1)
+    lay = B.MoELayer(L["W_gate"], L["W_mask"], torch.cat([L["W_gu"], L["Ws_gu"]]).contiguous(),
+                     torch.cat([L["W_dt"], L["Ws_dt"]]).contiguous(), 6)
+    y, R = lay(L["x"])
+    torch.cuda.synchronize()
+    y = y.float().cpu().numpy()
+    G = gpu_routing_host({k: v.cpu() for k, v in R.items()})
+    check_logits(G, L)
+    O = check_routing_exact(G, 6, lay.sizes["block_m"], 0.5, n_shared=1)
+    assert np.all(G["counts"][48:] == T)
+    check_y(y, L, 6, O, TOL[torch.bfloat16], sample_tokens(T, 64, seed=T))
 
 
 @pytest.mark.parametrize("E,K", [(8, 1), (8, 8), (60, 4), (64, 6), (256, 8), (130, 3)])
