@@ -391,6 +391,39 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         if constexpr (LV) read_frags(0, 0, 0);
+        if constexpr (MODE == MODE_DOWN) {
+            // down projection: the stage boundary after the stage's last slice
+            // of MFMAs.  Every load of a slot goes out in its first slices, so
+            // the waits count the same loads, which get one slice more to land;
+            // the first fragments of the next stage are then read after the
+            // barrier.  (Up projection, 32 stages per tile: 1-2% slower this
+            // way; down, 12 stages at I = 768: 4-5% faster.)
+            static_assert(DKK < KK, "a slot's loads precede its last slice");
+            for (int s = 0; s < nst; ++s) {
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (kk + 1 < KK) {
+                        if constexpr (LV) read_frags(s, kk + 1, (kk + 1) & 1);
+                        if constexpr (LV) wait_lgkm<MF + 4>();
+                    } else {
+                        if constexpr (LV) wait_lgkm<0>();
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    slice(t, LIVE, kk & 1, s, kk);
+                    if (kk + 1 == KK && s + 1 < nst) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (s + 2 < nst) wait_vmcnt<C::S_LOOP>();
+                        else wait_vmcnt<0>();
+                        asm volatile("" ::: "memory");
+                        __builtin_amdgcn_s_barrier();
+                        asm volatile("" ::: "memory");
+                        if constexpr (LV) read_frags(s + 1, 0, 0);
+                    }
+                }
+            }
+            return;
+        }
         for (int s = 0; s < nst; ++s) {
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
