@@ -29,12 +29,16 @@
 // conflict-free.
 //
 // Pipeline: the LDS reads of k-slice kk + 1 are issued before the MFMAs of
-// slice kk, across stage boundaries too, so LDS reads overlap MFMAs.  The
-// global->LDS loads of a stage are interleaved with the MFMAs of the stage
-// before (issued in a burst, they stall every wave on the address unit while
-// the matrix cores idle).  A stage boundary waits (explicit vmcnt: the
-// compiler does not track LDS written by global_load_lds) for the next stage
-// and meets the other waves at a barrier, which frees the buffers just read.
+// slice kk, so LDS reads overlap MFMAs.  The global->LDS loads of a stage are
+// interleaved with the MFMAs of the stage before (issued in a burst, they
+// stall every wave on the address unit while the matrix cores idle).  A
+// stage boundary waits (explicit vmcnt: the compiler does not track LDS
+// written by global_load_lds) for the next stage and meets the other waves
+// at a barrier, which frees the buffers just read.  The up projection places
+// the boundary before the stage's last slice of MFMAs (whose fragments are
+// already in registers), so the next stage's first fragment reads overlap
+// them; the down projection places it after that slice, which gives the
+// operand loads one slice more to land.
 //
 // Scheduling: a persistent grid of one workgroup per CU walks the tiles that
 // exist on the device (blocks * column tiles); the tiles are split into eight
