@@ -34,11 +34,10 @@
 // stall every wave on the address unit while the matrix cores idle).  A
 // stage boundary waits (explicit vmcnt: the compiler does not track LDS
 // written by global_load_lds) for the next stage and meets the other waves
-// at a barrier, which frees the buffers just read.  The up projection places
-// the boundary before the stage's last slice of MFMAs (whose fragments are
-// already in registers), so the next stage's first fragment reads overlap
-// them; the down projection places it after that slice, which gives the
-// operand loads one slice more to land.
+// at a barrier, which frees the buffers just read.  The boundary sits inside
+// the stage's last slice of MFMAs (whose fragments are already in
+// registers): halfway through it in the up projection, after it in the down
+// projection (main_loop), so the operand loads get 3.5 or 4 slices to land.
 //
 // Scheduling: a persistent grid of one workgroup per CU walks the tiles that
 // exist on the device (blocks * column tiles); the tiles are split into eight
@@ -358,7 +357,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
     // the matrix cores do)
     constexpr int PER = C::PER;
     constexpr int MPS = C::MPS;
-    auto slice = [&](const Tile &t, auto LIVE, int set, int s, int kk) {
+    auto slice = [&](const Tile &t, auto LIVE, int set, int s, int kk, int at, auto &&mid) {
 #pragma unroll
         for (int j = 0; j < MPS; ++j) {
             const int m = j >> 2, n = j & 3;
@@ -369,6 +368,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
                 issue(t, s, kk * PER + j / (MPS / PER));
                 __builtin_amdgcn_sched_barrier(0);
             }
+            if (j == at) mid();
         }
     };
 
@@ -395,62 +395,47 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         if constexpr (LV) read_frags(0, 0, 0);
-        if constexpr (MODE == MODE_DOWN) {
-            // down projection: the stage boundary after the stage's last slice
-            // of MFMAs.  Every load of a slot goes out in its first slices, so
-            // the waits count the same loads, which get one slice more to land;
-            // the first fragments of the next stage are then read after the
-            // barrier.  (Up projection, 32 stages per tile: 1-2% slower this
-            // way; down, 12 stages at I = 768: 4-5% faster.)
-            static_assert(DKK < KK, "a slot's loads precede its last slice");
-            for (int s = 0; s < nst; ++s) {
-#pragma unroll
-                for (int kk = 0; kk < KK; ++kk) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    if (kk + 1 < KK) {
-                        if constexpr (LV) read_frags(s, kk + 1, (kk + 1) & 1);
-                        if constexpr (LV) wait_lgkm<MF + 4>();
-                    } else {
-                        if constexpr (LV) wait_lgkm<0>();
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                    slice(t, LIVE, kk & 1, s, kk);
-                    if (kk + 1 == KK && s + 1 < nst) {
-                        __builtin_amdgcn_sched_barrier(0);
-                        if (s + 2 < nst) wait_vmcnt<C::S_LOOP>();
-                        else wait_vmcnt<0>();
-                        asm volatile("" ::: "memory");
-                        __builtin_amdgcn_s_barrier();
-                        asm volatile("" ::: "memory");
-                        if constexpr (LV) read_frags(s + 1, 0, 0);
-                    }
-                }
-            }
-            return;
-        }
+        // The stage boundary (the wait for the next stage's operands, the
+        // barrier, the first fragment reads of the next stage) sits inside
+        // the stage's last k-slice.  Every load of a slot goes out in the
+        // slot's first slices, so the waits count the same loads wherever
+        // the boundary sits.  Up projection (32 stages per tile at d =
+        // 2048): halfway through the last slice's MFMAs, so the loads get
+        // 3.5 slices to land and the slice's other half hides the next
+        // fragment reads (4% faster at keep 0.5, 1% at keep 1.0 than at the
+        // slice's start).  Down projection (12 stages at I = 768): after
+        // the slice, 4 slices to land (4-5% faster than at its start; the
+        // half-way point measured the same).
+        static_assert(DKK < KK, "a slot's loads precede its last slice");
+        constexpr int AT = MODE == MODE_UP ? MPS / 2 - 1 : MPS - 1;
         for (int s = 0; s < nst; ++s) {
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
                 __builtin_amdgcn_sched_barrier(0);
                 if (kk + 1 < KK) {
                     if constexpr (LV) read_frags(s, kk + 1, (kk + 1) & 1);
-                } else if (s + 1 < nst) {
-                    // stage boundary: stage s + 1 landed for every wave,
-                    // stage s read by every wave
+                    // the slice's own fragments are in (LDS reads complete
+                    // in order; only the MF + 4 reads of the next slice may
+                    // be pending)
+                    if constexpr (LV) wait_lgkm<MF + 4>();
+                } else {
+                    if constexpr (LV) wait_lgkm<0>();
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                const bool bnd = kk + 1 == KK && s + 1 < nst;
+                slice(t, LIVE, kk & 1, s, kk, AT, [&] {
+                    if (!bnd) return;
+                    // stage s + 1 landed for every wave, stage s read by
+                    // every wave (this slice's fragments are in registers)
+                    __builtin_amdgcn_sched_barrier(0);
                     if (s + 2 < nst) wait_vmcnt<C::S_LOOP>();
                     else wait_vmcnt<0>();
-                    if constexpr (LV) wait_lgkm<0>();
                     asm volatile("" ::: "memory");
                     __builtin_amdgcn_s_barrier();
                     asm volatile("" ::: "memory");
                     if constexpr (LV) read_frags(s + 1, 0, 0);
-                }
-                // the slice's own fragments are in (LDS reads complete in
-                // order; only the MF + 4 reads of the next slice may be
-                // pending)
-                if constexpr (LV) wait_lgkm<MF + 4>();
-                __builtin_amdgcn_sched_barrier(0);
-                slice(t, LIVE, kk & 1, s, kk);
+                    __builtin_amdgcn_sched_barrier(0);
+                });
             }
         }
     };
