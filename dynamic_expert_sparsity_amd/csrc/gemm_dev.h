@@ -408,6 +408,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
         // half-way point measured the same).
         static_assert(DKK < KK, "a slot's loads precede its last slice");
         constexpr int AT = MODE == MODE_UP ? MPS / 2 - 1 : MPS - 1;
+        static_assert(AT >= 0 && AT < MPS, "the boundary falls on one of the slice's MFMAs");
         for (int s = 0; s < nst; ++s) {
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
